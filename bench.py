@@ -1,0 +1,224 @@
+"""Benchmark of the 4-bit grouped MoE layer on one MI355X.
+
+One step = one full layer call (moe_route -> moe_grouped_gemm_q4 ->
+moe_combine) over the 512-token prefill workload (H 2048, I 512, 256 experts
+top-8 + 1 shared expert, 4-bit g64 weights), inputs resident in HBM.
+Prints ONE JSON line.  Secondary workloads (2048-token prefill, batch-1
+decode over 1000 tokens, skewed 8192-token prefill in chunks of 2048) are
+timed too and reported under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 MFMA
+EXPERT_BYTES_PER_WEIGHT = 0.5 + 4.0 / 64   # code nibble + bf16 scale and bias per 64
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def expert_bytes(H, I):
+    return int(3 * H * I * EXPERT_BYTES_PER_WEIGHT)
+
+
+def layer_flops(T, H, I, k, I_sh):
+    return 2.0 * (T * k * 3 * H * I + T * 3 * H * I_sh)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--block-rows", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of extra workloads to run")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps   # ms per call
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_grouped_amd as bq
+    from workload import CONFIGS, make_activations, make_weights
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS["prefill512"]
+    log("generating weights")
+    w = make_weights(cfg, seed=0)
+    layer = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
+    log("weights resident")
+
+    def prep(c):
+        xb, lg = make_activations(c)
+        return bq.bf16_from_bits(xb, dev), torch.from_numpy(lg).to(dev)
+
+    # ---------------- headline: prefill 512 ----------------
+    x, lg = prep(cfg)
+    T = cfg.T
+    step = lambda: layer.forward(x, lg)  # noqa: E731
+    ms = timed(step, args.steps, args.warmup, torch)
+    bufs = layer.buffers(T)
+    counts = bufs["routing"].counts.cpu().numpy()
+    touched = int(np.count_nonzero(counts))
+
+    # per-call durations (events on the launch stream around each ABI call)
+    r, ws_r, ws_g = bufs["routing"], bufs["route_ws"], bufs["gemm_ws"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev = evs[i]
+        ev[0].record()
+        bq.moe_route(lg, cfg.k, layer.block_rows, r, ws_r)
+        ev[1].record()
+        bq.moe_grouped_gemm_q4(x, cfg.I, cfg.I_sh, cfg.E, cfg.k, layer.block_rows, r,
+                               *layer.weight_mats(), bufs["expert_out"], bufs["shared_out"], ws_g)
+        ev[2].record()
+        bq.moe_combine(bufs["expert_out"], bufs["shared_out"], r, cfg.k, bufs["y"])
+        ev[3].record()
+    torch.cuda.synchronize()
+    t_route = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs])) * 1e-3
+    t_gemm = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in evs])) * 1e-3
+    t_comb = float(np.mean([ev[2].elapsed_time(ev[3]) for ev in evs])) * 1e-3
+
+    eb = expert_bytes(cfg.H, cfg.I)
+    gemm_bytes = (touched + 1) * eb + T * cfg.H * 2
+    layer_bytes = (touched + 1) * eb + T * cfg.H * 2 + T * cfg.E * 4 + T * cfg.H * 2
+    flops = layer_flops(T, cfg.H, cfg.I, cfg.k, cfg.I_sh)
+    t_layer = ms * 1e-3
+    t_roof = max(flops / MFMA_BF16_PEAK, layer_bytes / HBM_PEAK)
+    achieved = gemm_bytes / t_gemm
+    result = {
+        "metric": "MoE-layer tokens/s (prefill 512 tokens, 256 experts top-8 + shared, 4-bit g64)",
+        "value": T / t_layer,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill512", "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "k": cfg.k, "I_shared": cfg.I_sh, "block_rows": layer.block_rows,
+                   "weights": "4-bit codes, bf16 scale+bias per 64"},
+        "roofline": {"bound": "hbm", "kernel": "moe_grouped_gemm_q4 (gate/up+SwiGLU and down kernels)",
+                     "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None,
+                     "algorithmic_bytes": gemm_bytes, "avg_launch_us": t_gemm * 1e6},
+        "layer": {"route_us": t_route * 1e6, "gemm_us": t_gemm * 1e6, "combine_us": t_comb * 1e6,
+                  "touched_experts": touched, "layer_bytes": layer_bytes, "layer_flops": flops,
+                  "roofline_frac": t_roof / t_layer,
+                  "mfma_frac": flops / t_layer / MFMA_BF16_PEAK,
+                  "hbm_frac": layer_bytes / t_layer / HBM_PEAK},
+    }
+    log(f"prefill512: {ms*1e3:.1f} us/call, {T/t_layer:,.0f} tok/s, gemm {t_gemm*1e6:.1f} us "
+        f"({achieved/1e9:.0f} GB/s), route {t_route*1e6:.1f} us, combine {t_comb*1e6:.1f} us")
+
+    # ---------------- secondary workloads ----------------
+    extra = {}
+    only = set(filter(None, args.only.split(",")))
+    if not args.no_extra:
+        if not only or "prefill2048" in only:
+            c = CONFIGS["prefill2048"]
+            x2, lg2 = prep(c)
+            ms2 = timed(lambda: layer.forward(x2, lg2), max(10, args.steps // 4), 5, torch)
+            cnt = layer.buffers(c.T)["routing"].counts.cpu().numpy()
+            tch = int(np.count_nonzero(cnt))
+            fl = layer_flops(c.T, c.H, c.I, c.k, c.I_sh)
+            by = (tch + 1) * eb + c.T * c.H * 4 + c.T * c.E * 4
+            t = ms2 * 1e-3
+            extra["prefill2048"] = {"tokens_per_s": c.T / t, "us_per_call": ms2 * 1e3,
+                                    "mfma_frac": fl / t / MFMA_BF16_PEAK,
+                                    "roofline_frac": max(fl / MFMA_BF16_PEAK, by / HBM_PEAK) / t}
+            log(f"prefill2048: {ms2*1e3:.1f} us/call, {c.T/t:,.0f} tok/s, "
+                f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%")
+            del x2, lg2
+        if not only or "decode" in only:
+            c = CONFIGS["decode"]
+            xd, lgd = prep(c)
+            xs = [xd[i:i + 1] for i in range(c.T)]
+            ls = [lgd[i:i + 1] for i in range(c.T)]
+
+            def run_tokens():
+                for i in range(c.T):
+                    layer.forward(xs[i], ls[i])
+
+            msd = timed(run_tokens, 3, 1, torch)       # ms per 1000 tokens
+            t_tok = msd * 1e-3 / c.T
+            by_tok = 9 * eb + c.H * 4 + c.E * 4
+            extra["decode"] = {"tokens_per_s": 1.0 / t_tok, "us_per_token": t_tok * 1e6,
+                               "hbm_frac": by_tok / t_tok / HBM_PEAK,
+                               "note": "1000 single-token calls back to back, same layer (warm caches)"}
+            log(f"decode: {t_tok*1e6:.2f} us/token, HBM {100*by_tok/t_tok/HBM_PEAK:.1f}%")
+        if not only or "skew8192" in only:
+            c = CONFIGS["skew8192"]
+            xs_, lgs_ = prep(c)
+            y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+            ws = layer.forward_chunked(xs_, lgs_, c.chunk, y)
+            mss = timed(lambda: layer.forward_chunked(xs_, lgs_, c.chunk, y, ws), 10, 2, torch)
+            t = mss * 1e-3
+            fl = layer_flops(c.T, c.H, c.I, c.k, c.I_sh)
+            extra["skew8192"] = {"tokens_per_s": c.T / t, "us_per_8192": mss * 1e3,
+                                 "mfma_frac": fl / t / MFMA_BF16_PEAK}
+            log(f"skew8192: {mss*1e3:.1f} us per 4 chunks, {c.T/t:,.0f} tok/s, "
+                f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%")
+    result["extra"] = extra
+
+    # ---------------- CPU oracle baseline (rank 0, N = 1) ----------------
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        xb, lgn = make_activations(cfg)
+        t0 = time.perf_counter()
+        oracle.moe_layer(xb, lgn, w.gate, w.up, w.down, cfg.k, w.sh_gate, w.sh_up, w.sh_down)
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        result["cpu_baseline"] = {
+            "value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full 512-token layer call of the same workload ({dt:.1f} s; numpy fp64, "
+                      f"BLAS threads {threads}, elementwise work single-threaded)"}
+        log(f"cpu oracle: {dt:.1f} s for 512 tokens")
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,287 @@
+"""Python binding of the 4-bit grouped MoE layer's C ABI (include/moe_q4.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of libmoe_q4.so.  PyTorch is used for device memory and streams.  If the
+library has not been built this module raises on first use; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
+
+MOE_OK = 0
+MOE_ERR_NULL = -1
+MOE_ERR_SHAPE = -2
+MOE_ERR_ALIGN = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_HIP = -5
+MOE_ERR_UNIMPLEMENTED = -6
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+class MoeQ4Mat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_idx", "topk_w", "counts", "offsets", "sorted_assign", "assign_row",
+        "block_expert", "block_row", "n_blocks")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_S = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_abi_version": (_I, []),
+    "moe_status_str": (ctypes.c_char_p, [_I]),
+    "moe_route_max_blocks": (_I, [_I, _I, _I, _I]),
+    "moe_route_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "moe_route": (_I, [_P, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _S, _P]),
+    "moe_gemm_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
+    "moe_grouped_gemm_q4": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
+                            + [ctypes.POINTER(MoeQ4Mat)] * 6 + [_P, _P, _P, _S, _P]),
+    "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
+    "moe_layer_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
+    "moe_layer_chunked": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I]
+                          + [ctypes.POINTER(MoeQ4Mat)] * 6 + [_P, _P, _S, _P]),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+
+def lib():
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python bit_quantized_grouped_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# Device containers (plumbing: torch allocations + the C structs over them)
+# ---------------------------------------------------------------------------
+
+class DeviceQMat:
+    """One 4-bit matrix set [n_exp, N, K] resident on the device."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor):
+        self.codes, self.scales, self.biases = codes, scales, biases
+        self.struct = MoeQ4Mat(codes.data_ptr(), scales.data_ptr(), biases.data_ptr())
+
+    @classmethod
+    def from_host(cls, m, device) -> "DeviceQMat":
+        """m: object with numpy .codes uint32, .scales/.biases uint16."""
+        codes = torch.from_numpy(m.codes.view("int32")).to(device)
+        scales = torch.from_numpy(m.scales.view("int16")).to(device)
+        biases = torch.from_numpy(m.biases.view("int16")).to(device)
+        return cls(codes, scales, biases)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.biases))
+
+
+class DeviceRouting:
+    """Caller-owned routing output arrays for one layer call of T tokens."""
+
+    def __init__(self, T: int, E: int, k: int, block_rows: int, device):
+        self.T, self.E, self.k, self.block_rows = T, E, k, block_rows
+        self.max_blocks = route_max_blocks(T, E, k, block_rows)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.sorted_assign = torch.empty(T * k, **i32)
+        self.assign_row = torch.empty(T * k, **i32)
+        self.block_expert = torch.empty(self.max_blocks, **i32)
+        self.block_row = torch.empty(self.max_blocks, **i32)
+        self.n_blocks = torch.empty(1, **i32)
+        self.struct = MoeRouting(*[getattr(self, n).data_ptr() for n, _ in MoeRouting._fields_])
+
+    def to_host(self) -> dict:
+        return {n: getattr(self, n).cpu().numpy() for n, _ in MoeRouting._fields_}
+
+
+# ---------------------------------------------------------------------------
+# The C ABI, one Python function per entry point (same names)
+# ---------------------------------------------------------------------------
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def route_max_blocks(T, E, k, block_rows) -> int:
+    v = lib().moe_route_max_blocks(T, E, k, block_rows)
+    _check(min(v, 0), "moe_route_max_blocks")
+    return v
+
+
+def route_workspace_bytes(T, E, k, block_rows) -> int:
+    return lib().moe_route_workspace_bytes(T, E, k, block_rows)
+
+
+def gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows) -> int:
+    return lib().moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows)
+
+
+def layer_workspace_bytes(chunk_tokens, H, I, I_sh, E, k, block_rows) -> int:
+    return lib().moe_layer_workspace_bytes(chunk_tokens, H, I, I_sh, E, k, block_rows)
+
+
+def moe_route(logits: torch.Tensor, k: int, block_rows: int, routing: DeviceRouting,
+              ws: torch.Tensor, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route(_ptr(logits), T, E, k, block_rows, ctypes.byref(routing.struct),
+                           _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream, logits.device)), "moe_route")
+
+
+def _mat(m):
+    return None if m is None else ctypes.byref(m.struct)
+
+
+def moe_grouped_gemm_q4(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, block_rows: int,
+                        routing: DeviceRouting, gate, up, down, sh_gate, sh_up, sh_down,
+                        expert_out: torch.Tensor, shared_out, ws: torch.Tensor, stream=None):
+    T, H = x.shape
+    _check(lib().moe_grouped_gemm_q4(
+        _ptr(x), T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct),
+        _mat(gate), _mat(up), _mat(down), _mat(sh_gate), _mat(sh_up), _mat(sh_down),
+        _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream, x.device)), "moe_grouped_gemm_q4")
+
+
+def moe_combine(expert_out: torch.Tensor, shared_out, routing: DeviceRouting, k: int,
+                y: torch.Tensor, stream=None):
+    T, H = y.shape
+    _check(lib().moe_combine(_ptr(expert_out), _ptr(shared_out), ctypes.byref(routing.struct),
+                             T, H, k, _ptr(y), _stream(stream, y.device)), "moe_combine")
+
+
+def moe_layer_chunked(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
+                      block_rows: int, chunk_tokens: int, gate, up, down, sh_gate, sh_up,
+                      sh_down, y: torch.Tensor, ws: torch.Tensor, stream=None):
+    T, H = x.shape
+    E = logits.shape[1]
+    _check(lib().moe_layer_chunked(
+        _ptr(x), _ptr(logits), T, H, I, I_sh, E, k, block_rows, chunk_tokens,
+        _mat(gate), _mat(up), _mat(down), _mat(sh_gate), _mat(sh_up), _mat(sh_down),
+        _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream, x.device)),
+        "moe_layer_chunked")
+
+
+# ---------------------------------------------------------------------------
+# Convenience: one layer's device weights and buffers, running the three calls
+# ---------------------------------------------------------------------------
+
+def _bytes_tensor(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+class MoeLayer:
+    """Device-resident weights of one layer plus per-call buffers for T tokens."""
+
+    def __init__(self, weights, H: int, I: int, I_sh: int, E: int, k: int, device,
+                 block_rows: int = 32):
+        self.H, self.I, self.I_sh, self.E, self.k = H, I, I_sh, E, k
+        self.block_rows = block_rows
+        self.device = torch.device(device)
+        up = lambda m: None if m is None else DeviceQMat.from_host(m, self.device)  # noqa: E731
+        self.gate, self.up, self.down = up(weights.gate), up(weights.up), up(weights.down)
+        self.sh_gate, self.sh_up, self.sh_down = (up(weights.sh_gate), up(weights.sh_up),
+                                                  up(weights.sh_down))
+        self._bufs = {}
+
+    def weight_mats(self):
+        return (self.gate, self.up, self.down, self.sh_gate, self.sh_up, self.sh_down)
+
+    def buffers(self, T: int) -> dict:
+        if T not in self._bufs:
+            d = self.device
+            b = dict(
+                routing=DeviceRouting(T, self.E, self.k, self.block_rows, d),
+                route_ws=_bytes_tensor(route_workspace_bytes(T, self.E, self.k, self.block_rows), d),
+                gemm_ws=_bytes_tensor(gemm_workspace_bytes(T, self.H, self.I, self.I_sh, self.E,
+                                                           self.k, self.block_rows), d),
+                expert_out=torch.empty((T * self.k, self.H), dtype=torch.bfloat16, device=d),
+                shared_out=(torch.empty((T, self.H), dtype=torch.bfloat16, device=d)
+                            if self.I_sh else None),
+                y=torch.empty((T, self.H), dtype=torch.bfloat16, device=d),
+            )
+            self._bufs[T] = b
+        return self._bufs[T]
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, out: torch.Tensor | None = None,
+                stream=None) -> dict:
+        """route -> grouped GEMM -> combine on one stream; returns the buffers used."""
+        T = x.shape[0]
+        b = self.buffers(T)
+        y = b["y"] if out is None else out
+        moe_route(logits, self.k, self.block_rows, b["routing"], b["route_ws"], stream)
+        moe_grouped_gemm_q4(x, self.I, self.I_sh, self.E, self.k, self.block_rows, b["routing"],
+                            *self.weight_mats(), b["expert_out"], b["shared_out"], b["gemm_ws"],
+                            stream)
+        moe_combine(b["expert_out"], b["shared_out"], b["routing"], self.k, y, stream)
+        return dict(b, y=y)
+
+    def forward_chunked(self, x, logits, chunk_tokens: int, y: torch.Tensor, ws=None, stream=None):
+        T = x.shape[0]
+        if ws is None:
+            ws = _bytes_tensor(layer_workspace_bytes(min(chunk_tokens, T), self.H, self.I,
+                                                     self.I_sh, self.E, self.k, self.block_rows),
+                               self.device)
+        moe_layer_chunked(x, logits, self.I, self.I_sh, self.k, self.block_rows, chunk_tokens,
+                          *self.weight_mats(), y, ws, stream)
+        return ws
+
+
+def bf16_from_bits(bits_np, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns (numpy) -> bf16 device tensor (a reinterpreting copy)."""
+    return torch.from_numpy(bits_np.view("int16")).to(device).view(torch.bfloat16)
+
+
+def bf16_to_bits(t: torch.Tensor):
+    """bf16 tensor -> uint16 numpy bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")

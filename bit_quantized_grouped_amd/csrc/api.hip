@@ -1,0 +1,295 @@
+// C ABI of the 4-bit grouped MoE layer: host-side validation, workspace
+// layout and kernel dispatch.  Every entry point validates first and
+// enqueues nothing on failure; none allocates, frees or synchronises.
+#include <new>
+
+#include "../../include/moe_q4.h"
+#include "moe_launch.h"
+
+using namespace moeq4;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxE = 1024;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_block_rows(int br) { return br == 16 || br == 32 || br == 64; }
+
+int check_route_shape(int T, int E, int k, int block_rows) {
+    if (T < 1 || E < 1 || E > kMaxE || k < 1 || k > E) return MOE_ERR_SHAPE;
+    if (!valid_block_rows(block_rows)) return MOE_ERR_SHAPE;
+    if ((long long)T * k >= (1ll << 30)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int check_layer_shape(int T, int H, int I, int I_sh, int E, int k, int block_rows) {
+    const int st = check_route_shape(T, E, k, block_rows);
+    if (st) return st;
+    if (H < 64 || H % 64 || I < 64 || I % 64 || I_sh < 0 || I_sh % 64) return MOE_ERR_SHAPE;
+    const long long widest = H > I ? H : I;
+    if ((long long)T * k * widest >= (1ll << 31)) return MOE_ERR_SHAPE;
+    if ((long long)T * (I_sh > H ? I_sh : H) >= (1ll << 31)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int check_mat(const moe_q4_mat* m) {
+    if (!m || !m->codes || !m->scales || !m->biases) return MOE_ERR_NULL;
+    if (!aligned(m->codes, 16) || !aligned(m->scales, 2) || !aligned(m->biases, 2))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+int check_routing(const moe_routing* r) {
+    if (!r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->sorted_assign ||
+        !r->assign_row || !r->block_expert || !r->block_row || !r->n_blocks)
+        return MOE_ERR_NULL;
+    return MOE_OK;
+}
+
+int max_blocks_of(int T, int E, int k, int br) {
+    const long long n = (long long)T * k;
+    return (int)((n + br - 1) / br + (E < n ? E : n));
+}
+
+RoutingDev to_dev(const moe_routing* r) {
+    return RoutingDev{r->topk_idx, r->topk_w,        r->counts,       r->offsets,  r->sorted_assign,
+                      r->assign_row, r->block_expert, r->block_row, r->n_blocks};
+}
+
+QMatDev to_dev(const moe_q4_mat* m) {
+    if (!m) return QMatDev{nullptr, nullptr, nullptr};
+    return QMatDev{m->codes, m->scales, m->biases};
+}
+
+// Layout of moe_layer_chunked's workspace for chunks of C tokens.
+struct LayerWs {
+    size_t topk_idx, topk_w, counts, offsets, sorted_assign, assign_row, block_expert, block_row,
+        n_blocks, route_ws, gemm_ws, expert_out, shared_out, total;
+    size_t route_bytes, gemm_bytes;
+};
+
+LayerWs layer_ws_layout(int C, int H, int I, int I_sh, int E, int k, int br) {
+    LayerWs L{};
+    const size_t n = (size_t)C * k;
+    const size_t mb = (size_t)max_blocks_of(C, E, k, br);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += align_up(bytes, 256);
+        return at;
+    };
+    L.topk_idx = take(n * 4);
+    L.topk_w = take(n * 4);
+    L.counts = take((size_t)E * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.sorted_assign = take(n * 4);
+    L.assign_row = take(n * 4);
+    L.block_expert = take(mb * 4);
+    L.block_row = take(mb * 4);
+    L.n_blocks = take(4);
+    size_t a, b;
+    L.route_bytes = route_ws_layout(C, E, k, &a, &b);
+    L.route_ws = take(L.route_bytes);
+    L.gemm_bytes = gemm_ws_layout(C, I, I_sh, k, &a, &b);
+    L.gemm_ws = take(L.gemm_bytes);
+    L.expert_out = take(n * H * 2);
+    L.shared_out = take(I_sh ? (size_t)C * H * 2 : 0);
+    L.total = o;
+    return L;
+}
+
+int gemm_args_ok(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k, int block_rows,
+                 const moe_routing* r, const moe_q4_mat* gate, const moe_q4_mat* up,
+                 const moe_q4_mat* down, const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                 const moe_q4_mat* sh_down, const uint16_t* expert_out,
+                 const uint16_t* shared_out) {
+    int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
+    if (st) return st;
+    if (!x || !expert_out) return MOE_ERR_NULL;
+    if ((st = check_routing(r))) return st;
+    if ((st = check_mat(gate)) || (st = check_mat(up)) || (st = check_mat(down))) return st;
+    if (I_sh) {
+        if (!shared_out) return MOE_ERR_NULL;
+        if ((st = check_mat(sh_gate)) || (st = check_mat(sh_up)) || (st = check_mat(sh_down)))
+            return st;
+        if (!aligned(shared_out, 16)) return MOE_ERR_ALIGN;
+    } else if (sh_gate || sh_up || sh_down || shared_out) {
+        return MOE_ERR_SHAPE;   // shared matrices given but I_sh == 0
+    }
+    if (!aligned(x, 16) || !aligned(expert_out, 16)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return kAbiVersion; }
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "null pointer";
+        case MOE_ERR_SHAPE: return "bad shape";
+        case MOE_ERR_ALIGN: return "misaligned pointer";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch error";
+        case MOE_ERR_UNIMPLEMENTED: return "unimplemented";
+        default: return "unknown status";
+    }
+}
+
+int moe_route_max_blocks(int T, int E, int k, int block_rows) {
+    const int st = check_route_shape(T, E, k, block_rows);
+    if (st) return st;
+    return max_blocks_of(T, E, k, block_rows);
+}
+
+size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows) {
+    if (check_route_shape(T, E, k, block_rows)) return 0;
+    size_t a, b;
+    return route_ws_layout(T, E, k, &a, &b);
+}
+
+int moe_route(const float* logits, int T, int E, int k, int block_rows, const moe_routing* out,
+              void* ws, size_t ws_bytes, hipStream_t stream) {
+    try {
+        int st = check_route_shape(T, E, k, block_rows);
+        if (st) return st;
+        if (!logits || !ws) return MOE_ERR_NULL;
+        if ((st = check_routing(out))) return st;
+        if (!aligned(logits, 4) || !aligned(ws, 256)) return MOE_ERR_ALIGN;
+        if (ws_bytes < moe_route_workspace_bytes(T, E, k, block_rows)) return MOE_ERR_WORKSPACE;
+        const hipError_t e = launch_route(logits, T, E, k, block_rows,
+                                          max_blocks_of(T, E, k, block_rows), to_dev(out), ws,
+                                          stream);
+        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+size_t moe_gemm_workspace_bytes(int T, int H, int I, int I_sh, int E, int k, int block_rows) {
+    if (check_layer_shape(T, H, I, I_sh, E, k, block_rows)) return 0;
+    size_t a, b;
+    return gemm_ws_layout(T, I, I_sh, k, &a, &b);
+}
+
+int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
+                        int block_rows, const moe_routing* r, const moe_q4_mat* gate,
+                        const moe_q4_mat* up, const moe_q4_mat* down, const moe_q4_mat* sh_gate,
+                        const moe_q4_mat* sh_up, const moe_q4_mat* sh_down, uint16_t* expert_out,
+                        uint16_t* shared_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    try {
+        int st = gemm_args_ok(x, T, H, I, I_sh, E, k, block_rows, r, gate, up, down, sh_gate,
+                              sh_up, sh_down, expert_out, shared_out);
+        if (st) return st;
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
+        if (ws_bytes < moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))
+            return MOE_ERR_WORKSPACE;
+        GemmProblem p{};
+        p.x = x;
+        p.T = T;
+        p.H = H;
+        p.I = I;
+        p.I_sh = I_sh;
+        p.E = E;
+        p.k = k;
+        p.block_rows = block_rows;
+        p.max_blocks = max_blocks_of(T, E, k, block_rows);
+        p.r = to_dev(r);
+        p.gate = to_dev(gate);
+        p.up = to_dev(up);
+        p.down = to_dev(down);
+        p.sh_gate = to_dev(sh_gate);
+        p.sh_up = to_dev(sh_up);
+        p.sh_down = to_dev(sh_down);
+        p.expert_out = expert_out;
+        p.shared_out = shared_out;
+        const hipError_t e = launch_grouped_gemm(p, ws, stream);
+        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const moe_routing* r,
+                int T, int H, int k, uint16_t* y, hipStream_t stream) {
+    try {
+        if (T < 1 || k < 1 || H < 64 || H % 64) return MOE_ERR_SHAPE;
+        if ((long long)T * k * H >= (1ll << 31)) return MOE_ERR_SHAPE;
+        if (!expert_out || !y || !r || !r->assign_row || !r->topk_w) return MOE_ERR_NULL;
+        if (!aligned(expert_out, 16) || !aligned(y, 16) || (shared_out && !aligned(shared_out, 16)))
+            return MOE_ERR_ALIGN;
+        const hipError_t e =
+            launch_combine(expert_out, shared_out, r->assign_row, r->topk_w, T, H, k, y, stream);
+        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+size_t moe_layer_workspace_bytes(int chunk_tokens, int H, int I, int I_sh, int E, int k,
+                                 int block_rows) {
+    if (check_layer_shape(chunk_tokens, H, I, I_sh, E, k, block_rows)) return 0;
+    return layer_ws_layout(chunk_tokens, H, I, I_sh, E, k, block_rows).total;
+}
+
+int moe_layer_chunked(const uint16_t* x, const float* logits, int T, int H, int I, int I_sh,
+                      int E, int k, int block_rows, int chunk_tokens, const moe_q4_mat* gate,
+                      const moe_q4_mat* up, const moe_q4_mat* down, const moe_q4_mat* sh_gate,
+                      const moe_q4_mat* sh_up, const moe_q4_mat* sh_down, uint16_t* y, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+    try {
+        if (chunk_tokens < 1) return MOE_ERR_SHAPE;
+        const int C = chunk_tokens < T ? chunk_tokens : T;
+        int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
+        if (st) return st;
+        if ((st = check_layer_shape(C, H, I, I_sh, E, k, block_rows))) return st;
+        if (!x || !logits || !y || !ws) return MOE_ERR_NULL;
+        if ((st = check_mat(gate)) || (st = check_mat(up)) || (st = check_mat(down))) return st;
+        if (I_sh) {
+            if ((st = check_mat(sh_gate)) || (st = check_mat(sh_up)) || (st = check_mat(sh_down)))
+                return st;
+        } else if (sh_gate || sh_up || sh_down) {
+            return MOE_ERR_SHAPE;
+        }
+        if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, 256))
+            return MOE_ERR_ALIGN;
+        const LayerWs L = layer_ws_layout(C, H, I, I_sh, E, k, block_rows);
+        if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        char* base = (char*)ws;
+        moe_routing r{};
+        r.topk_idx = (int32_t*)(base + L.topk_idx);
+        r.topk_w = (float*)(base + L.topk_w);
+        r.counts = (int32_t*)(base + L.counts);
+        r.offsets = (int32_t*)(base + L.offsets);
+        r.sorted_assign = (int32_t*)(base + L.sorted_assign);
+        r.assign_row = (int32_t*)(base + L.assign_row);
+        r.block_expert = (int32_t*)(base + L.block_expert);
+        r.block_row = (int32_t*)(base + L.block_row);
+        r.n_blocks = (int32_t*)(base + L.n_blocks);
+        uint16_t* eo = (uint16_t*)(base + L.expert_out);
+        uint16_t* so = I_sh ? (uint16_t*)(base + L.shared_out) : nullptr;
+        for (int t0 = 0; t0 < T; t0 += C) {
+            const int Tc = (T - t0) < C ? (T - t0) : C;
+            st = moe_route(logits + (size_t)t0 * E, Tc, E, k, block_rows, &r, base + L.route_ws,
+                           L.route_bytes, stream);
+            if (st) return st;
+            st = moe_grouped_gemm_q4(x + (size_t)t0 * H, Tc, H, I, I_sh, E, k, block_rows, &r,
+                                     gate, up, down, sh_gate, sh_up, sh_down, eo, so,
+                                     base + L.gemm_ws, L.gemm_bytes, stream);
+            if (st) return st;
+            st = moe_combine(eo, so, &r, Tc, H, k, y + (size_t)t0 * H, stream);
+            if (st) return st;
+        }
+        return MOE_OK;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+}  // extern "C"

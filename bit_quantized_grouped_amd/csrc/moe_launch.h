@@ -1,0 +1,54 @@
+// Internal host-side interface between the C ABI (api.hip) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq4 {
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct QMatDev {
+    const uint32_t* codes;
+    const uint16_t* scales;
+    const uint16_t* biases;
+};
+
+struct RoutingDev {
+    int32_t* topk_idx;
+    float* topk_w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_assign;
+    int32_t* assign_row;
+    int32_t* block_expert;
+    int32_t* block_row;
+    int32_t* n_blocks;
+};
+
+// route.hip
+int route_tokens_per_wg(int T, int k);
+size_t route_ws_layout(int T, int E, int k, size_t* off_hist, size_t* off_rank);
+hipError_t launch_route(const float* logits, int T, int E, int k, int block_rows, int max_blocks,
+                        const RoutingDev& r, void* ws, hipStream_t stream);
+
+// gemm_q4.hip
+struct GemmProblem {
+    const uint16_t* x;
+    int T, H, I, I_sh, E, k, block_rows, max_blocks;
+    RoutingDev r;
+    QMatDev gate, up, down, sh_gate, sh_up, sh_down;
+    uint16_t* expert_out;
+    uint16_t* shared_out;
+};
+size_t gemm_ws_layout(int T, int I, int I_sh, int k, size_t* off_h, size_t* off_hsh);
+hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const uint16_t* expert_out, const uint16_t* shared_out,
+                          const int32_t* assign_row, const float* topk_w, int T, int H, int k,
+                          uint16_t* y, hipStream_t stream);
+
+}  // namespace moeq4

@@ -1,0 +1,175 @@
+/*
+ * moe_q4.h - C ABI of the 4-bit grouped MoE layer for MI355X (gfx950).
+ *
+ * The layer: a router picks k of E experts per token and one shared expert
+ * sees every token; each expert is a SwiGLU FFN whose weights are 4-bit
+ * groupwise-affine codes (one bf16 scale and one bf16 bias per 64 weights).
+ * Sources, by page and section:
+ *   [P1] dothoosh.com, "Perplexity Lily: 1.35x faster decode for Qwen3.6 on
+ *        Apple silicon": "Model specification" (256 experts, 8 selected plus
+ *        a shared expert) and "Prefill optimizations" (fused dequantization
+ *        in the grouped GEMM with FP32 accumulation; GPU-resident routing
+ *        histogram, prefix scan, scatter and block map with no CPU sync;
+ *        32-row tiles; bounded prefill chunks);
+ *   [P3] droneth.or.th post on Lily: "A big model that touches only part of
+ *        its weights per token" (format, bf16 expansion, ablations) and
+ *        "Decode is limited by bandwidth more than by compute" (batch-1
+ *        decode is bound by bytes moved).
+ *
+ * Conventions for every call below
+ *   - All array pointers are DEVICE pointers owned by the caller, except the
+ *     small argument structs themselves, which are HOST pointers read during
+ *     the call only.  The caller keeps every buffer alive until the work
+ *     enqueued on `stream` has finished.  Outputs must not alias inputs.
+ *   - Every call only validates its arguments on the host and enqueues
+ *     kernels on `stream`; it never allocates, frees or synchronises the
+ *     host, and never reads device memory on the host.  Device-side values
+ *     (such as n_blocks) stay on the device.
+ *   - A failed call returns a negative status and enqueues nothing.  No C++
+ *     exception crosses this boundary.  Device data (code words, scale
+ *     values) is not validated.
+ *   - The library holds no mutable global state: calls on different streams
+ *     may run concurrently from different threads if their buffers differ.
+ *   - Shapes: 1 <= k <= E <= 1024; H, I, I_sh are multiples of 64 (I_sh = 0
+ *     means no shared expert); T >= 1; T*k*max(H, I) < 2^31;
+ *     block_rows is 16, 32 or 64.
+ *   - Inputs are finite.  Scales must satisfy |s| < 2^118 (the kernels work
+ *     with 512*s internally).
+ *   - bf16 values travel as their uint16 bit patterns.
+ */
+#ifndef MOE_Q4_H
+#define MOE_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK                 0
+#define MOE_ERR_NULL          -1  /* a required pointer is NULL */
+#define MOE_ERR_SHAPE         -2  /* a size or block_rows outside the limits above */
+#define MOE_ERR_ALIGN         -3  /* codes, x, y, expert_out or shared_out not 16-byte aligned,
+                                     or a workspace not 256-byte aligned */
+#define MOE_ERR_WORKSPACE     -4  /* workspace smaller than the matching *_workspace_bytes() */
+#define MOE_ERR_HIP           -5  /* a kernel launch failed (hipGetLastError) */
+#define MOE_ERR_UNIMPLEMENTED -6  /* combination not built into this library */
+
+/* One set of 4-bit matrices [n_exp, N, K] (row-major, K innermost):
+ *   codes  uint32 [n_exp, N, K/8]: code of weight (n, 8c+i) in bits 4i..4i+3
+ *          of word c (lowest k in the low nibble); 16-byte aligned;
+ *   scales bf16   [n_exp, N, K/64]: scale of weights (n, 64g .. 64g+63);
+ *   biases bf16   [n_exp, N, K/64].
+ * Weight value: w = bf16_rne(fp32(q * scale + bias)) ([P1] "Prefill
+ * optimizations"; [P3] "A big model ...").  Gate and up are [E, I, H],
+ * down is [E, H, I]; the shared expert's are [1, I_sh, H] and [1, H, I_sh]. */
+typedef struct {
+    const uint32_t* codes;
+    const uint16_t* scales;
+    const uint16_t* biases;
+} moe_q4_mat;
+
+/* Routing results of one layer call (all device arrays, caller-allocated).
+ * Assignment a = t*k + j is token t's j-th expert.  [P1] "Prefill
+ * optimizations" (histogram, prefix scan, scatter, block map); [P3] ablations.
+ *   topk_idx      int32 [T, k]  experts by descending logit, ties -> lower index
+ *   topk_w        fp32  [T, k]  softmax over the k selected logits
+ *   counts        int32 [E]     assignments per expert (histogram)
+ *   offsets       int32 [E+1]   exclusive prefix sum of counts; offsets[E] = T*k
+ *   sorted_assign int32 [T*k]   row -> a, rows grouped by expert, ascending a inside one
+ *   assign_row    int32 [T*k]   a -> row (inverse permutation)
+ *   block_expert  int32 [max_blocks]  expert of row block b (-1 past n_blocks)
+ *   block_row     int32 [max_blocks]  first row of block b (-1 past n_blocks)
+ *   n_blocks      int32 [1]     number of blocks, written on the device
+ * Block map: for e ascending, i < ceil(counts[e]/block_rows), block
+ * (e, offsets[e] + block_rows*i) covering min(block_rows, counts[e] - block_rows*i) rows. */
+typedef struct {
+    int32_t* topk_idx;
+    float*   topk_w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_assign;
+    int32_t* assign_row;
+    int32_t* block_expert;
+    int32_t* block_row;
+    int32_t* n_blocks;
+} moe_routing;
+
+/* Version of this ABI (bumped on any signature change). */
+int moe_abi_version(void);
+
+/* Human-readable text of a status code (static string; never NULL). */
+const char* moe_status_str(int status);
+
+/* max_blocks = ceil(T*k / block_rows) + min(E, T*k): the length of
+ * block_expert / block_row.  Returns a negative status on bad shapes. */
+int moe_route_max_blocks(int T, int E, int k, int block_rows);
+
+/* Device workspace bytes moe_route needs (0 on bad shapes). */
+size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows);
+
+/* GPU-resident routing ([P1] "Prefill optimizations", GPU-resident routing
+ * bullet; [P1] "Model specification"; [P3] "A big model ...").
+ *   logits  fp32 [T, E] router scores (device, 4-byte aligned, finite)
+ *   out     host struct of device arrays described at moe_routing
+ *   ws      device workspace of at least moe_route_workspace_bytes() bytes
+ * Outputs are bit-exact functions of the logits (topk_w within fp32 rounding). */
+int moe_route(const float* logits, int T, int E, int k, int block_rows,
+              const moe_routing* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Device workspace bytes moe_grouped_gemm_q4 needs (0 on bad shapes). */
+size_t moe_gemm_workspace_bytes(int T, int H, int I, int I_sh, int E, int k, int block_rows);
+
+/* Grouped expert GEMM with 4-bit dequantization fused into the tiles
+ * ([P1] "Prefill optimizations", fused-dequantization bullet; [P3] "A big
+ * model ...": weights expanded to bf16 tile by tile, FP32 accumulation,
+ * expanded weights never written to memory).
+ *   x          bf16 [T, H] activations (16-byte aligned)
+ *   r          routing from moe_route with the same T, E, k, block_rows
+ *   gate, up   [E, I, H] 4-bit matrices; down [E, H, I]
+ *   sh_*       shared expert [1, I_sh, H] / [1, H, I_sh]; all NULL iff I_sh == 0
+ *   expert_out bf16 [T*k, H]: row r = FFN of expert block_expert for token
+ *              sorted_assign[r]/k, unweighted: (silu(x Wg^T) * (x Wu^T)) Wd^T
+ *   shared_out bf16 [T, H]: shared expert FFN of every token (NULL iff I_sh == 0)
+ *   ws         device workspace of at least moe_gemm_workspace_bytes() bytes
+ * Accumulation is FP32; the SwiGLU activations and outputs are rounded to bf16. */
+int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
+                        int block_rows, const moe_routing* r,
+                        const moe_q4_mat* gate, const moe_q4_mat* up, const moe_q4_mat* down,
+                        const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                        const moe_q4_mat* sh_down,
+                        uint16_t* expert_out, uint16_t* shared_out,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted combine: y[t] = sum_j topk_w[t,j] * expert_out[assign_row[t*k+j]]
+ * + shared_out[t], summed in fp32 in slot order with the shared expert last
+ * (weight 1; the pages name no shared-expert gate), rounded once to bf16.
+ * shared_out may be NULL (no shared expert).  y bf16 [T, H], 16-byte aligned. */
+int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const moe_routing* r,
+                int T, int H, int k, uint16_t* y, hipStream_t stream);
+
+/* Device workspace bytes moe_layer_chunked needs for chunks of chunk_tokens. */
+size_t moe_layer_workspace_bytes(int chunk_tokens, int H, int I, int I_sh, int E, int k,
+                                 int block_rows);
+
+/* Bounded-chunk driver ([P1] "Prefill optimizations", memory bullet: long
+ * prompts run in bounded chunks so temporaries stay small).  Tokens
+ * [c*chunk_tokens, ...) form independent layer calls (route, grouped GEMM,
+ * combine) enqueued in order on `stream` with no host synchronisation.
+ * All temporaries (routing, h, expert_out, shared_out) live in `ws` and are
+ * sized for one chunk.  y bf16 [T, H]. */
+int moe_layer_chunked(const uint16_t* x, const float* logits, int T, int H, int I, int I_sh,
+                      int E, int k, int block_rows, int chunk_tokens,
+                      const moe_q4_mat* gate, const moe_q4_mat* up, const moe_q4_mat* down,
+                      const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                      const moe_q4_mat* sh_down,
+                      uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_Q4_H */

@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every function include/moe_q4.h declares,
+and rejects bad arguments on the host with the documented status codes
+(no GPU needed: these paths return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_grouped_amd as bq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe_q4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 10
+    L = bq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(bq.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert bq.abi_version() == 1
+    for st, txt in [(0, "ok"), (-1, "null pointer"), (-2, "bad shape"), (-3, "misaligned pointer"),
+                    (-4, "workspace too small"), (-5, "HIP launch error"), (-6, "unimplemented"),
+                    (-99, "unknown status")]:
+        assert bq.status_str(st) == txt
+
+
+def test_max_blocks_and_workspace_sizes():
+    assert bq.route_max_blocks(512, 256, 8, 32) == 128 + 256
+    assert bq.route_max_blocks(2048, 256, 8, 32) == 512 + 256
+    assert bq.route_max_blocks(1, 256, 8, 32) == 1 + 8
+    assert bq.route_max_blocks(64, 16, 2, 32) == 4 + 16
+    assert bq.lib().moe_route_max_blocks(1, 256, 8, 48) == bq.MOE_ERR_SHAPE
+    assert bq.route_workspace_bytes(512, 256, 8, 32) > 0
+    assert bq.route_workspace_bytes(0, 256, 8, 32) == 0
+    # h (T*k x I) + shared h (T x I_sh), bf16
+    assert bq.gemm_workspace_bytes(512, 2048, 512, 512, 256, 8, 32) >= 512 * 8 * 512 * 2 + 512 * 512 * 2
+    assert bq.gemm_workspace_bytes(512, 2000, 512, 512, 256, 8, 32) == 0
+    assert bq.layer_workspace_bytes(2048, 2048, 512, 512, 256, 8, 32) > 2048 * 8 * 2048 * 2
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)          # never dereferenced: validation fails first
+MISALIGNED = P(0x10008)
+
+
+def _routing(ptr=FAKE):
+    return bq.MoeRouting(*([ptr.value] * 9))
+
+
+def _mat(codes=FAKE):
+    return bq.MoeQ4Mat(codes.value, FAKE.value, FAKE.value)
+
+
+def test_route_rejects_bad_arguments():
+    L = bq.lib()
+    r = _routing()
+    ok_ws = bq.route_workspace_bytes(64, 16, 2, 32)
+    assert L.moe_route(None, 64, 16, 2, 32, ctypes.byref(r), FAKE, ok_ws, None) == bq.MOE_ERR_NULL
+    assert L.moe_route(FAKE, 64, 16, 2, 32, None, FAKE, ok_ws, None) == bq.MOE_ERR_NULL
+    bad = bq.MoeRouting(*([FAKE.value] * 8 + [None]))
+    assert L.moe_route(FAKE, 64, 16, 2, 32, ctypes.byref(bad), FAKE, ok_ws, None) == bq.MOE_ERR_NULL
+    for T, E, k, br in [(0, 16, 2, 32), (64, 16, 17, 32), (64, 16, 0, 32), (64, 2000, 2, 32),
+                        (64, 16, 2, 8), (64, 16, 2, 128)]:
+        assert L.moe_route(FAKE, T, E, k, br, ctypes.byref(r), FAKE, 1 << 30, None) == bq.MOE_ERR_SHAPE
+    assert L.moe_route(FAKE, 64, 16, 2, 32, ctypes.byref(r), FAKE, ok_ws - 1, None) == bq.MOE_ERR_WORKSPACE
+    assert L.moe_route(P(0x10002), 64, 16, 2, 32, ctypes.byref(r), FAKE, ok_ws, None) == bq.MOE_ERR_ALIGN
+
+
+def test_gemm_rejects_bad_arguments():
+    L = bq.lib()
+    r = _routing()
+    m = _mat()
+    ws = bq.gemm_workspace_bytes(64, 256, 128, 128, 16, 2, 32)
+
+    def call(x=FAKE, T=64, H=256, I=128, I_sh=128, E=16, k=2, br=32, mats=None, eo=FAKE, so=FAKE,
+             wsb=ws):
+        mats = mats or [m] * 6
+        args = [x, T, H, I, I_sh, E, k, br, ctypes.byref(r)]
+        args += [ctypes.byref(q) if q is not None else None for q in mats]
+        args += [eo, so, FAKE, wsb, None]
+        return L.moe_grouped_gemm_q4(*args)
+
+    assert call(x=None) == bq.MOE_ERR_NULL
+    assert call(eo=None) == bq.MOE_ERR_NULL
+    assert call(so=None) == bq.MOE_ERR_NULL
+    assert call(H=200) == bq.MOE_ERR_SHAPE
+    assert call(I=96) == bq.MOE_ERR_SHAPE
+    assert call(I_sh=32) == bq.MOE_ERR_SHAPE
+    assert call(I_sh=0, so=None) == bq.MOE_ERR_SHAPE    # shared matrices passed without I_sh
+    assert call(mats=[_mat(MISALIGNED)] + [m] * 5) == bq.MOE_ERR_ALIGN
+    assert call(x=P(0x10004)) == bq.MOE_ERR_ALIGN
+    assert call(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
+    nul = bq.MoeQ4Mat(FAKE.value, None, FAKE.value)
+    assert call(mats=[m, nul, m, m, m, m]) == bq.MOE_ERR_NULL
+
+
+def test_combine_and_chunked_reject_bad_arguments():
+    L = bq.lib()
+    r = _routing()
+    assert L.moe_combine(None, None, ctypes.byref(r), 4, 256, 2, FAKE, None) == bq.MOE_ERR_NULL
+    assert L.moe_combine(FAKE, None, ctypes.byref(r), 4, 100, 2, FAKE, None) == bq.MOE_ERR_SHAPE
+    assert L.moe_combine(FAKE, None, ctypes.byref(r), 4, 256, 2, MISALIGNED, None) == bq.MOE_ERR_ALIGN
+    m = _mat()
+    mats = [ctypes.byref(m)] * 6
+    ws = bq.layer_workspace_bytes(32, 256, 128, 128, 16, 2, 32)
+    args = lambda chunk, wsb: [FAKE, FAKE, 64, 256, 128, 128, 16, 2, 32, chunk] + mats + [FAKE, FAKE, wsb, None]  # noqa: E731
+    assert L.moe_layer_chunked(*args(0, ws)) == bq.MOE_ERR_SHAPE
+    assert L.moe_layer_chunked(*args(32, ws - 1)) == bq.MOE_ERR_WORKSPACE

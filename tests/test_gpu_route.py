@@ -1,0 +1,92 @@
+"""GPU routing parity: every routing array bit-exact against the oracle
+(topk_w within 1e-6), on all five workloads and on tie-heavy / edge cases."""
+import numpy as np
+import pytest
+
+from gpu_cases import announce, assert_routing_matches, gpu_route, require_gpu
+from workload import CONFIGS, make_activations
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_route_parity_workloads(name):
+    cfg = CONFIGS[name]
+    _, logits = make_activations(cfg)
+    T = cfg.call_tokens
+    starts = [0]
+    if cfg.per_token:
+        starts = list(range(0, 24))             # first 24 decode tokens, one call each
+    elif cfg.chunk:
+        starts = list(range(0, cfg.T, cfg.chunk))
+    for t0 in starts:
+        announce(f"route {name} t0={t0} T={T}")
+        L = logits[t0:t0 + T]
+        assert_routing_matches(gpu_route(L, cfg.k, 32), L, cfg.k, 32)
+
+
+@pytest.mark.parametrize("block_rows", [16, 32, 64])
+def test_route_block_rows(block_rows):
+    _, logits = make_activations(CONFIGS["prefill512"])
+    announce(f"route prefill512 block_rows={block_rows}")
+    assert_routing_matches(gpu_route(logits, 8, block_rows), logits, 8, block_rows)
+
+
+def test_route_deterministic_repeat():
+    _, logits = make_activations(CONFIGS["prefill2048"])
+    announce("route prefill2048 x3 determinism")
+    runs = [gpu_route(logits, 8, 32) for _ in range(3)]
+    for r in runs[1:]:
+        for key in runs[0]:
+            assert np.array_equal(runs[0][key], r[key]), key
+
+
+def _tie_heavy(T, E, levels, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.integers(0, levels, (T, E)).astype(np.float32) / np.float32(4)) - np.float32(1)
+
+
+@pytest.mark.parametrize("T,E,k,levels,seed", [
+    (300, 256, 8, 3, 1),       # heavy ties over 256 experts
+    (77, 64, 6, 2, 2),         # two values only
+    (33, 16, 16, 4, 3),        # k = E
+    (1, 256, 8, 5, 4),         # single token
+    (129, 100, 7, 3, 5),       # E not a multiple of 64
+    (40, 1000, 8, 6, 6),       # E up to 1000 (16 experts per lane)
+    (5, 1, 1, 1, 7),           # one expert
+])
+def test_route_ties(T, E, k, levels, seed):
+    L = _tie_heavy(T, E, levels, seed)
+    announce(f"route ties T={T} E={E} k={k}")
+    assert_routing_matches(gpu_route(L, k, 32), L, k, 32)
+
+
+def test_route_all_equal_and_signed_zero():
+    L = np.zeros((50, 32), np.float32)
+    L[::2, 3] = np.float32(-0.0)
+    L[1::2, 7] = np.float32(-0.0)
+    announce("route equal logits / signed zeros")
+    got = gpu_route(L, 4, 32)
+    assert_routing_matches(got, L, 4, 32)
+    assert got["topk_idx"].tolist() == [[0, 1, 2, 3]] * 50
+
+
+@pytest.mark.parametrize("counts", [[0, 31, 32, 33, 64, 1, 0, 2], [0, 0, 0, 97, 0, 0, 0, 0],
+                                    [16, 16, 16, 16, 16, 16, 16, 16]])
+def test_route_exact_counts(counts):
+    # k = 1 and a dominant logit per token force the histogram exactly
+    E = len(counts)
+    rng = np.random.default_rng(9)
+    owner = np.repeat(np.arange(E), counts)
+    rng.shuffle(owner)
+    L = rng.standard_normal((owner.size, E)).astype(np.float32)
+    L[np.arange(owner.size), owner] = np.float32(10.0)
+    announce(f"route exact counts {counts}")
+    got = gpu_route(L, 1, 32)
+    assert got["counts"].tolist() == counts
+    assert_routing_matches(got, L, 1, 32)
