@@ -13,7 +13,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
+# MOE_Q4_LIB may name another build of the same library (e.g. other tile sizes)
+LIB_PATH = os.environ.get("MOE_Q4_LIB") or os.path.join(HERE, "libmoe_q4.so")
 
 MOE_OK = 0
 MOE_ERR_NULL = -1

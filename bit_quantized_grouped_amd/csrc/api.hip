@@ -11,7 +11,7 @@ using namespace moeq4;
 namespace {
 
 constexpr int kAbiVersion = 1;
-constexpr int kMaxE = 1024;
+constexpr int kMaxE = 1000;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -158,10 +158,11 @@ int moe_route(const float* logits, int T, int E, int k, int block_rows, const mo
     try {
         int st = check_route_shape(T, E, k, block_rows);
         if (st) return st;
-        if (!logits || !ws) return MOE_ERR_NULL;
+        const size_t need = moe_route_workspace_bytes(T, E, k, block_rows);
+        if (!logits || (need && !ws)) return MOE_ERR_NULL;
         if ((st = check_routing(out))) return st;
         if (!aligned(logits, 4) || !aligned(ws, 256)) return MOE_ERR_ALIGN;
-        if (ws_bytes < moe_route_workspace_bytes(T, E, k, block_rows)) return MOE_ERR_WORKSPACE;
+        if (ws_bytes < need) return MOE_ERR_WORKSPACE;
         const hipError_t e = launch_route(logits, T, E, k, block_rows,
                                           max_blocks_of(T, E, k, block_rows), to_dev(out), ws,
                                           stream);

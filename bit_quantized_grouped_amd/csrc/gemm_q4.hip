@@ -6,33 +6,82 @@
 // memory).
 //
 // One kernel template serves both projections:
-//   NMAT = 2  gate and up over the same 16 output columns per wave, SwiGLU
-//             epilogue h = silu(g) * u -> bf16 h  (A = x rows gathered by token)
+//   NMAT = 2  gate and up over the same output columns, SwiGLU epilogue
+//             h = silu(g) * u -> bf16 h  (A = x rows gathered by token)
 //   NMAT = 1  down projection -> bf16 expert_out / shared_out
 //             (A = h rows, contiguous in sorted-row order)
-// Work unit = one row block of the block map (MT rows of one expert) x 64
-// output columns (4 waves x 16).  The shared expert is an extra dense group
-// over all tokens, as the first sh_blocks slots of grid.y.
+// Work item = one row block of the block map (MT rows of one expert) x
+// COLS = 4 waves x NSUB x 16 output columns.  The shared expert is an extra
+// dense group over all tokens, as the first sh_blocks row blocks.
 //
 // Data path per K-chunk of KC:
-//   A: the block's MT rows x KC bf16 are staged in LDS (row stride KC+8 to
-//      keep ds_read_b128 conflict free) and read once per MFMA by every wave;
-//   B: each lane loads KC/32 consecutive code words of one weight row
-//      straight from HBM into registers (4 lanes cover a row's KC/2 bytes
-//      contiguously), dequantizes one word (8 weights) at a time to bf16 in
-//      registers and feeds it to v_mfma_f32_16x16x32_bf16.  A lane's 8
-//      weights are the 8 consecutive k of one code word, so the K order
-//      inside each MFMA is the natural one for both operands.
+//   A: the block's MT rows x KC bf16 are fetched DEPTH-1 chunks ahead into
+//      registers, then staged in LDS (double-buffered, row stride KC+8 so
+//      ds_read_b128 is conflict free) and read by every wave;
+//   B: each lane streams KC/32 consecutive code words of each of its weight
+//      rows straight from HBM into registers with buffer loads (4 lanes
+//      cover a row's KC/2 bytes contiguously; the chunk and subtile offsets
+//      ride in the scalar offset, so no per-load address arithmetic),
+//      DEPTH-1 chunks ahead of the math.  Each word (8 weights) is dequantized
+//      in registers to bf16 and fed to v_mfma_f32_16x16x32_bf16.  A lane's 8
+//      weights are the 8 consecutive k of its word, so both operands use the
+//      natural K order inside each MFMA.
+//   Epilogue: accumulators -> bf16 tile in LDS -> 16-byte row stores.
 #include "moe_device.h"
 #include "moe_launch.h"
 
+// Tile shape per projection: NSUB 16-column subtiles per wave, the largest
+// K-chunk (a divisor of K is used), and the number of chunks of code words in
+// flight per wave (register pipeline depth).
+#ifndef MOE_GU_WAVES
+#define MOE_GU_WAVES 4
+#endif
+#ifndef MOE_GU_NSUB
+#define MOE_GU_NSUB 1
+#endif
+#ifndef MOE_GU_KC
+#define MOE_GU_KC 128
+#endif
+#ifndef MOE_GU_DEPTH
+#define MOE_GU_DEPTH 4
+#endif
+#ifndef MOE_DN_WAVES
+#define MOE_DN_WAVES 4
+#endif
+#ifndef MOE_DN_NSUB
+#define MOE_DN_NSUB 2
+#endif
+#ifndef MOE_DN_KC
+#define MOE_DN_KC 128
+#endif
+#ifndef MOE_DN_DEPTH
+#define MOE_DN_DEPTH 4
+#endif
+// Resident workgroups per CU are capped by reserving LDS (0 = no cap): with
+// equal work items, the item count over resident slots sets how full the
+// last dispatch round is.
+#ifndef MOE_GU_WG_PER_CU
+#define MOE_GU_WG_PER_CU 0
+#endif
+#ifndef MOE_DN_WG_PER_CU
+#define MOE_DN_WG_PER_CU 0
+#endif
+
 namespace moeq4 {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes); loads past the end return 0.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 
 struct GroupedArgs {
     const uint16_t* a_routed;
     const uint16_t* a_shared;
     int lda_routed, lda_shared;
-    int gather;            // routed A rows: 1 -> token sorted_assign[row]/k, 0 -> row itself
+    int rows_routed, rows_shared;   // rows of the A arrays (bounds of the A resources)
+    int gather;                     // routed A rows: 1 -> token sorted_assign[row]/k, 0 -> row
     int k;
     int T;
     const int32_t* sorted_assign;
@@ -44,25 +93,127 @@ struct GroupedArgs {
     QMatDev rB[2];
     QMatDev sB[2];
     int N, K, N_sh, K_sh;
+    int n_tiles;                    // column tiles per row block (of the wider of N, N_sh)
     uint16_t* out_routed;
     uint16_t* out_shared;
 };
 
-template <int NMAT, int MT, int KC>
-__global__ __launch_bounds__(256) void grouped_q4_kernel(GroupedArgs p) {
+// Work item -> workgroup.  Workgroups are dispatched round-robin over the
+// 8 XCDs (each with its own L2), so workgroup L runs on XCD L % 8.  The
+// valid items (a count known only on the device) are split into 8
+// contiguous ranges, one per XCD: the column tiles of one row block, and
+// consecutive blocks of one expert, then share an L2.
+constexpr int kXcds = 8;
+
+template <int NMAT, int NSUB, int W>
+struct BChunk {
+    u32x4_t w[NMAT][NSUB][W / 4 > 0 ? W / 4 : 1];
+    u32x2_t w2[NMAT][NSUB];           // used when W == 2
+};
+
+template <int NMAT, int NSUB, int KC>
+struct Streams {
+    rsrc_t codes[NMAT];
+    int voff_c;                       // per-lane byte offset (row, lane group)
+    int sub_c;                        // byte stride of 16 rows in codes
+};
+
+template <int NMAT, int NSUB, int KC>
+__device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32>& B,
+                                       const Streams<NMAT, NSUB, KC>& S, int c) {
+    constexpr int W = KC / 32;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            const int so_c = s * S.sub_c + c * (KC / 2);
+            if constexpr (W >= 4) {
+#pragma unroll
+                for (int j = 0; j < W / 4; ++j)
+                    B.w[m][s][j] = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(S.codes[m], S.voff_c + 16 * j,
+                                                                        so_c, 0));
+            } else {
+                B.w2[m][s] = __builtin_bit_cast(
+                    u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(S.codes[m], S.voff_c, so_c, 0));
+            }
+        }
+}
+
+template <int NMAT, int NSUB, int W>
+__device__ __forceinline__ uint32_t word_of(const BChunk<NMAT, NSUB, W>& B, int m, int s, int j) {
+    if constexpr (W >= 4) return B.w[m][s][j / 4][j % 4];
+    else return B.w2[m][s][j];
+}
+
+// sSc / sBi: this lane's row of bf16 scales / biases in LDS (row stride GS,
+// matrix stride mstride); grp = the group of the lane's words in this chunk.
+template <int NMAT, int MT, int KC, int NSUB>
+__device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32>& B,
+                                              const uint16_t* sAc, const uint16_t* sSc,
+                                              const uint16_t* sBi, int GS, int mstride, int grp,
+                                              float unit_inv, int nl, int g, int msub_act,
+                                              f32x4_t (&acc)[NMAT][NSUB][MT / 16]) {
+    constexpr int W = KC / 32;
+    constexpr int LDA = KC + 8;
+    float sc[NMAT][NSUB], bi[NMAT][NSUB];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            const int at = m * mstride + s * 16 * GS + grp;
+            sc[m][s] = bf16_to_f32(sSc[at]) * unit_inv;
+            bi[m][s] = bf16_to_f32(sBi[at]);
+        }
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        bf16x8_t bw[NMAT][NSUB];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s)
+                bw[m][s] = dequant_word(word_of(B, m, s, j), sc[m][s], bi[m][s]);
+#pragma unroll
+        for (int mi = 0; mi < MT / 16; ++mi) {
+            if (mi > 0 && mi >= msub_act) break;   // 16-row subtiles past the block's rows
+            const bf16x8_t a = *(const bf16x8_t*)(sAc + (mi * 16 + nl) * LDA + 8 * (g * W + j));
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int s = 0; s < NSUB; ++s)
+                    acc[m][s][mi] = mfma_16x16x32(a, bw[m][s], acc[m][s][mi]);
+        }
+    }
+}
+
+template <int NMAT, int MT, int KC, int NSUB, int DEPTH, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
+    constexpr int NT = WAVES * 64;   // threads
     constexpr int W = KC / 32;       // code words per lane per chunk
     constexpr int MSUB = MT / 16;
     constexpr int LDA = KC + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sA[MT * LDA];
+    constexpr int ROWS = WAVES * NSUB * 16;        // weight rows (output columns) per matrix
+    constexpr int COLS = ROWS;
+    constexpr int A_PIECES = MT * (KC / 8);        // 16-byte pieces of the A tile per chunk
+    constexpr int APT = (A_PIECES + NT - 1) / NT;  // per thread
+    // LDS: [A buffer 0][A buffer 1][scale|bias pairs]; the output tile reuses it at the end
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem_g[];
     __shared__ int s_row[MT];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int nl = lane & 15, g = lane >> 4;
-    const int slot = blockIdx.y;
+
+    // ---- work item ----
+    const int n_items = (p.sh_blocks + p.n_blocks[0]) * p.n_tiles;
+    const int per = (n_items + kXcds - 1) / kXcds;
+    const int xcd = blockIdx.x % kXcds, seq = blockIdx.x / kXcds;
+    const int item = xcd * per + seq;
+    if (seq >= per || item >= n_items) return;
+    const int slot = item / p.n_tiles, tile = item % p.n_tiles;
     const bool is_sh = slot < p.sh_blocks;
 
-    int r0, nr, N, K, lda, expert = 0;
+    int r0, nr, N, K, lda, a_rows, expert = 0;
     const uint16_t* A;
     uint16_t* out;
     if (is_sh) {
@@ -72,10 +223,10 @@ __global__ __launch_bounds__(256) void grouped_q4_kernel(GroupedArgs p) {
         K = p.K_sh;
         A = p.a_shared;
         lda = p.lda_shared;
+        a_rows = p.rows_shared;
         out = p.out_shared;
     } else {
         const int b = slot - p.sh_blocks;
-        if (b >= p.n_blocks[0]) return;
         expert = p.block_expert[b];
         r0 = p.block_row[b];
         nr = min(MT, p.offsets[expert + 1] - r0);
@@ -83,95 +234,171 @@ __global__ __launch_bounds__(256) void grouped_q4_kernel(GroupedArgs p) {
         K = p.K;
         A = p.a_routed;
         lda = p.lda_routed;
+        a_rows = p.rows_routed;
         out = p.out_routed;
     }
-    if ((int)blockIdx.x * 64 >= N) return;   // uniform per workgroup
+    const int n_base = tile * COLS;
+    if (n_base >= N) return;   // uniform per workgroup
+    const int G = K / 64;      // scale groups per weight row
+    const int GS = G + 8;      // padded LDS row stride (16-byte rows, conflict-free lane reads)
+
+    uint16_t* sA = smem_g;
+    uint16_t* sSc = smem_g + 2 * MT * LDA;          // [NMAT][ROWS][GS] scales
+    uint16_t* sBi = sSc + NMAT * ROWS * GS;         // [NMAT][ROWS][GS] biases
 
     if (tid < MT) {
         const int rr = min(tid, nr - 1);   // padding rows repeat the last row; never stored
         s_row[tid] = (is_sh || !p.gather) ? r0 + rr : p.sorted_assign[r0 + rr] / p.k;
     }
 
-    const int n = blockIdx.x * 64 + wave * 16 + nl;   // this lane's weight row
-    const uint32_t* bc[NMAT];
-    const uint16_t* bs[NMAT];
-    const uint16_t* bb[NMAT];
+    // ---- scale/bias pairs of the tile's ROWS rows, all K, into LDS ----
+    // (rows are contiguous in the scale arrays: 16-byte coalesced loads;
+    //  rows past N fall outside the buffer resource and read as zero)
+    Streams<NMAT, NSUB, KC> S;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
         const QMatDev& q = is_sh ? p.sB[m] : p.rB[m];
-        const size_t row = (size_t)expert * N + n;
-        bc[m] = q.codes + row * (K / 8) + g * W;
-        bs[m] = q.scales + row * (K / 64);
-        bb[m] = q.biases + row * (K / 64);
+        const size_t rows0 = (size_t)expert * N;
+        S.codes[m] = make_rsrc(q.codes + rows0 * (K / 8), (uint32_t)N * (K / 2));
+        const rsrc_t rs_s = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
+        const rsrc_t rs_b = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
+        const int pieces = ROWS * G / 8;
+        uint16_t* dsc = sSc + m * ROWS * GS;
+        uint16_t* dbi = sBi + m * ROWS * GS;
+        for (int pc = tid; pc < pieces; pc += NT) {
+            const int voff = (n_base * G + pc * 8) * 2;
+            const u32x4_t vs = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_s, voff, 0, 0));
+            const u32x4_t vb = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, voff, 0, 0));
+            if ((G & 7) == 0) {   // a piece is 8 groups of one row
+                const int row = (pc * 8) / G, grp = (pc * 8) % G;
+                *(u32x4_t*)(dsc + row * GS + grp) = vs;
+                *(u32x4_t*)(dbi + row * GS + grp) = vb;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int flat = pc * 8 + e;
+                    const int row = flat / G, grp = flat % G;
+                    dsc[row * GS + grp] = (uint16_t)(vs[e / 2] >> (16 * (e & 1)));
+                    dbi[row * GS + grp] = (uint16_t)(vb[e / 2] >> (16 * (e & 1)));
+                }
+            }
+        }
     }
+    const int row_lane = wave * NSUB * 16 + nl;     // lane's row within the tile
+    S.voff_c = (n_base + row_lane) * (K / 2) + g * W * 4;
+    S.sub_c = 16 * (K / 2);
+    const int lane_grp = (g * (KC / 4)) / 64;
+    const uint16_t* sSc_lane = sSc + row_lane * GS + lane_grp;
+    const uint16_t* sBi_lane = sBi + row_lane * GS + lane_grp;
+    const int mstride = ROWS * GS;
     const float unit_inv = 1.0f / fp8_unit();
+    const int msub_act = (nr + 15) / 16;
 
-    f32x4_t acc[NMAT][MSUB];
+    f32x4_t acc[NMAT][NSUB][MSUB];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int i = 0; i < MSUB; ++i) acc[m][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+            for (int i = 0; i < MSUB; ++i) acc[m][s][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();
+    __syncthreads();   // s_row
+    const rsrc_t a_rs = make_rsrc(A, (uint32_t)a_rows * lda * 2);
+    int a_voff[APT], a_lds[APT];
+    bool a_ok[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int q = tid + NT * i;
+        a_ok[i] = q < A_PIECES;
+        const int qq = a_ok[i] ? q : 0;
+        const int row = qq / (KC / 8), c8 = qq % (KC / 8);
+        a_voff[i] = s_row[row] * lda * 2 + c8 * 16;
+        a_lds[i] = row * LDA + c8 * 8;
+    }
+    auto load_a = [&](u32x4_t (&dst)[APT], int c) {
+#pragma unroll
+        for (int i = 0; i < APT; ++i)
+            if (a_ok[i])
+                dst[i] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff[i], c * KC * 2, 0));
+    };
+    auto store_a = [&](const u32x4_t (&src)[APT], uint16_t* dst) {
+#pragma unroll
+        for (int i = 0; i < APT; ++i)
+            if (a_ok[i]) *(u32x4_t*)(dst + a_lds[i]) = src[i];
+    };
+
     const int nchunks = K / KC;
-    for (int c = 0; c < nchunks; ++c) {
-        uint32_t wv[NMAT][W];
-        float s[NMAT], bz[NMAT];
-        const int grp = (c * KC + g * (KC / 4)) / 64;
+    // Register pipeline over K-chunks: the A rows and code words of chunk c
+    // live in Aq/Bq[c % DEPTH] and are requested DEPTH-1 chunks before the
+    // chunk's math, so no load latency sits between two barriers.  A chunk c
+    // is staged into LDS buffer c % 2 one chunk ahead of its math.
+    BChunk<NMAT, NSUB, W> Bq[DEPTH];
+    u32x4_t Aq[DEPTH][APT];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-            const uint32_t* src = bc[m] + c * (KC / 8);
-            if constexpr (W >= 4) {
+    for (int d = 0; d < DEPTH - 1; ++d)
+        if (d < nchunks) {
+            load_a(Aq[d], d);
+            load_b<NMAT, NSUB, KC>(Bq[d], S, d);
+        }
+    store_a(Aq[0], sA);
+    __syncthreads();
+    for (int c0 = 0; c0 < nchunks; c0 += DEPTH) {
 #pragma unroll
-                for (int j = 0; j < W; j += 4) {
-                    const u32x4_t v = *(const u32x4_t*)(src + j);
-                    wv[m][j] = v[0];
-                    wv[m][j + 1] = v[1];
-                    wv[m][j + 2] = v[2];
-                    wv[m][j + 3] = v[3];
-                }
-            } else {
-                const u32x2_t v = *(const u32x2_t*)src;
-                wv[m][0] = v[0];
-                wv[m][1] = v[1];
+        for (int d = 0; d < DEPTH; ++d) {
+            const int c = c0 + d;
+            if (c >= nchunks) break;
+            if (c + DEPTH - 1 < nchunks) {
+                load_a(Aq[(d + DEPTH - 1) % DEPTH], c + DEPTH - 1);
+                load_b<NMAT, NSUB, KC>(Bq[(d + DEPTH - 1) % DEPTH], S, c + DEPTH - 1);
             }
-            s[m] = bf16_to_f32(bs[m][grp]) * unit_inv;
-            bz[m] = bf16_to_f32(bb[m][grp]);
+            compute_chunk<NMAT, MT, KC, NSUB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane, sBi_lane, GS,
+                                              mstride, c * KC / 64, unit_inv, nl, g, msub_act, acc);
+            if (c + 1 < nchunks) store_a(Aq[(d + 1) % DEPTH], sA + ((c + 1) & 1) * MT * LDA);
+            __syncthreads();
         }
-        for (int q = tid; q < MT * (KC / 8); q += 256) {
-            const int row = q / (KC / 8), c8 = q % (KC / 8);
-            const u32x4_t v = *(const u32x4_t*)(A + (size_t)s_row[row] * lda + c * KC + c8 * 8);
-            *(u32x4_t*)(sA + row * LDA + c8 * 8) = v;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            bf16x8_t bw[NMAT];
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) bw[m] = dequant_word(wv[m][j], s[m], bz[m]);
-#pragma unroll
-            for (int mi = 0; mi < MSUB; ++mi) {
-                const bf16x8_t a = *(const bf16x8_t*)(sA + (mi * 16 + nl) * LDA + 8 * (g * W + j));
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m) acc[m][mi] = mfma_16x16x32(a, bw[m], acc[m][mi]);
-            }
-        }
-        __syncthreads();
     }
 
+    // ---- epilogue: bf16 tile [MT][COLS] in LDS, then 16-byte row stores ----
+    uint16_t* sO = smem_g;
 #pragma unroll
-    for (int mi = 0; mi < MSUB; ++mi) {
+    for (int s = 0; s < NSUB; ++s) {
+        const int col = (wave * NSUB + s) * 16 + nl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = mi * 16 + 4 * g + i;
-            if (row < nr) {
+        for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = mi * 16 + 4 * g + i;
                 float v;
-                if constexpr (NMAT == 2) v = silu_f32(acc[0][mi][i]) * acc[1][mi][i];
-                else v = acc[0][mi][i];
-                out[(size_t)(r0 + row) * N + n] = __builtin_bit_cast(uint16_t, (__bf16)v);
+                if constexpr (NMAT == 2) v = silu_f32(acc[0][s][mi][i]) * acc[1][s][mi][i];
+                else v = acc[0][s][mi][i];
+                sO[row * COLS + col] = __builtin_bit_cast(uint16_t, (__bf16)v);
             }
-        }
     }
+    __syncthreads();
+    constexpr int PIECES = MT * COLS / 8;
+    const int ncols = min(COLS, N - n_base);
+    for (int q = tid; q < PIECES; q += NT) {
+        const int row = q / (COLS / 8), c8 = (q % (COLS / 8)) * 8;
+        if (row < nr && c8 < ncols)
+            *(u32x4_t*)(out + (size_t)(r0 + row) * N + n_base + c8) =
+                *(const u32x4_t*)(sO + row * COLS + c8);
+    }
+}
+
+// Dynamic LDS bytes of one grouped_q4_kernel instance for K-groups G.
+template <int NMAT, int MT, int KC, int NSUB, int WAVES>
+static size_t grouped_lds_bytes(int G, int wg_per_cu) {
+    constexpr int LDA = KC + 8;
+    constexpr int ROWS = WAVES * NSUB * 16;
+    const size_t a = (size_t)2 * MT * LDA * 2 + (size_t)2 * NMAT * ROWS * (G + 8) * 2;
+    const size_t o = (size_t)MT * ROWS * 2;
+    size_t bytes = a > o ? a : o;
+    if (wg_per_cu > 0) {
+        const size_t cap = (size_t)160 * 1024 / (wg_per_cu + 1) + 1024;   // > 1/(n+1) of the CU's LDS
+        if (bytes < cap) bytes = cap;
+    }
+    return bytes;
 }
 
 size_t gemm_ws_layout(int T, int I, int I_sh, int k, size_t* off_h, size_t* off_hsh) {
@@ -183,24 +410,34 @@ size_t gemm_ws_layout(int T, int I, int I_sh, int k, size_t* off_h, size_t* off_
     return o;
 }
 
-static int pick_kc(int K, int K2) {
-    for (int kc = 256; kc >= 64; kc >>= 1)
+static int pick_kc(int K, int K2, int kc_max) {
+    for (int kc = kc_max; kc >= 64; kc >>= 1)
         if (K % kc == 0 && (K2 == 0 || K2 % kc == 0)) return kc;
     return 0;
 }
 
-template <int NMAT, int MT>
-static void launch_mt(const GroupedArgs& a, int kc, dim3 grid, hipStream_t stream) {
-    if (kc == 256) grouped_q4_kernel<NMAT, MT, 256><<<grid, 256, 0, stream>>>(a);
-    else if (kc == 128) grouped_q4_kernel<NMAT, MT, 128><<<grid, 256, 0, stream>>>(a);
-    else grouped_q4_kernel<NMAT, MT, 64><<<grid, 256, 0, stream>>>(a);
+template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES>
+static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_cu,
+                      hipStream_t stream) {
+#define MOE_LAUNCH(KCV)                                                                          \
+    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES><<<                                      \
+        grid, WAVES * 64, grouped_lds_bytes<NMAT, MT, KCV, NSUB, WAVES>(G, wg_per_cu), stream>>>(a)
+    if (kc == 256) MOE_LAUNCH(256);
+    else if (kc == 128) MOE_LAUNCH(128);
+    else MOE_LAUNCH(64);
+#undef MOE_LAUNCH
 }
 
-template <int NMAT>
-static void launch_grouped(const GroupedArgs& a, int mt, int kc, dim3 grid, hipStream_t stream) {
-    if (mt == 16) launch_mt<NMAT, 16>(a, kc, grid, stream);
-    else if (mt == 32) launch_mt<NMAT, 32>(a, kc, grid, stream);
-    else launch_mt<NMAT, 64>(a, kc, grid, stream);
+template <int NMAT, int NSUB, int DEPTH, int WAVES>
+static void launch_grouped(GroupedArgs a, int mt, int kc, int n_max, int slots, int G,
+                           int wg_per_cu, hipStream_t stream) {
+    constexpr int cols = WAVES * NSUB * 16;
+    a.n_tiles = (n_max + cols - 1) / cols;
+    const long long items = (long long)slots * a.n_tiles;
+    const int grid = (int)((items + kXcds - 1) / kXcds) * kXcds;
+    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES>(a, kc, grid, G, wg_per_cu, stream);
+    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES>(a, kc, grid, G, wg_per_cu, stream);
+    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES>(a, kc, grid, G, wg_per_cu, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t stream) {
@@ -220,12 +457,13 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t strea
     a.n_blocks = p.r.n_blocks;
     a.offsets = p.r.offsets;
     a.sh_blocks = sh_blocks;
-    const dim3 grid_y(1, sh_blocks + p.max_blocks);
+    const int slots = sh_blocks + p.max_blocks;
 
     // gate + up with SwiGLU: A = x (gathered), N = I, K = H
     a.a_routed = p.x;
     a.a_shared = p.x;
     a.lda_routed = a.lda_shared = p.H;
+    a.rows_routed = a.rows_shared = p.T;
     a.gather = 1;
     a.rB[0] = p.gate;
     a.rB[1] = p.up;
@@ -237,17 +475,17 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t strea
     a.K_sh = p.H;
     a.out_routed = h;
     a.out_shared = h_sh;
-    {
-        const int nmax = p.I > p.I_sh ? p.I : p.I_sh;
-        const dim3 grid(nmax / 64, grid_y.y);
-        launch_grouped<2>(a, mt, pick_kc(p.H, 0), grid, stream);
-    }
+    launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES>(
+        a, mt, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh, slots, p.H / 64,
+        MOE_GU_WG_PER_CU, stream);
 
     // down: A = h rows (contiguous), N = H, K = I
     a.a_routed = h;
     a.a_shared = h_sh;
     a.lda_routed = p.I;
     a.lda_shared = p.I_sh;
+    a.rows_routed = p.T * p.k;
+    a.rows_shared = p.T;
     a.gather = 0;
     a.rB[0] = p.down;
     a.sB[0] = p.sh_down;
@@ -257,10 +495,9 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t strea
     a.K_sh = p.I_sh;
     a.out_routed = p.expert_out;
     a.out_shared = p.shared_out;
-    {
-        const dim3 grid(p.H / 64, grid_y.y);
-        launch_grouped<1>(a, mt, pick_kc(p.I, p.I_sh), grid, stream);
-    }
+    launch_grouped<1, MOE_DN_NSUB, MOE_DN_DEPTH, MOE_DN_WAVES>(
+        a, mt, pick_kc(p.I, p.I_sh, MOE_DN_KC), p.H, slots,
+        (p.I > p.I_sh ? p.I : p.I_sh) / 64, MOE_DN_WG_PER_CU, stream);
     return hipGetLastError();
 }
 

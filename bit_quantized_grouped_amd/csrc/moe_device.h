@@ -63,8 +63,9 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float silu_f32(float z) {
-    return z / (1.0f + __expf(-z));
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
 template <typename T>

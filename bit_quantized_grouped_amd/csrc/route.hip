@@ -3,138 +3,181 @@
 // ([P1] dothoosh.com Lily article, "Prefill optimizations", GPU-resident
 // routing bullet; [P1] "Model specification": 256 experts, 8 selected).
 //
-// Three kernels on one stream:
-//   route_topk   one wave per token: k rounds of wave arg-max over the
-//                logits (ties to the lower expert), softmax over the k
-//                chosen; then, per workgroup, a histogram of its
-//                assignments and each assignment's rank among the
-//                workgroup's earlier assignments to the same expert
-//                (ballot match, scanned 64 assignments at a time, so the
-//                rank order is ascending assignment index: a stable sort).
-//   route_scan   one workgroup: per expert, the exclusive prefix over
-//                workgroups (-> each workgroup's first row for that
-//                expert), the totals (counts), their exclusive scan
-//                (offsets), and the block map with the device-side n_blocks.
-//   route_scatter  row = base[wg][e] + rank: sorted_assign and assign_row.
+// Two phases, each a device function:
+//   topk_token   one wave per token.  Logits become order-preserving
+//                integer keys; a radix select over the key bits (ballot +
+//                popcount per bit, stopping as soon as exactly k keys lie
+//                at or above the running threshold) finds the k-th largest
+//                value; ties at that value go to the lowest expert indices.
+//                The k chosen are ranked (value descending, index
+//                ascending) through LDS, and their softmax weights formed.
+//   group_all    one workgroup of 16 waves over the T*k assignments, cut
+//                into 16 contiguous segments.  Pass 1: per-segment expert
+//                histograms (ballot match of equal experts inside 64-lane
+//                chunks, one LDS update per distinct expert).  Then per
+//                expert: prefix over segments, totals (counts), exclusive
+//                scan (offsets) and the block map with n_blocks.  Pass 2
+//                re-walks the segments; each assignment's row is its
+//                segment's base for its expert plus its rank among equal
+//                experts earlier in the chunk: a stable counting sort.
+// Large T: a top-k kernel with one wave per token, then a one-workgroup
+// grouping kernel.  Small T: both phases in one workgroup (one launch).
 // Every output is a deterministic function of the logits.
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moeq4 {
 
-constexpr int kRouteThreads = 256;
-constexpr int kRouteWaves = kRouteThreads / WAVE;
+constexpr int kTopkWaves = 4;          // tokens per workgroup in the top-k kernel
+constexpr int kGroupThreads = 1024;    // one grouping workgroup: 16 waves
+constexpr int kGroupWaves = kGroupThreads / WAVE;
+constexpr int kFusedMaxTokens = 64;    // T at or below this: one fused launch
 
-template <int EPL>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int tok_per_wg,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ wg_hist, int32_t* __restrict__ local_rank) {
-    extern __shared__ int32_t smem[];
-    int32_t* s_exp = smem;                         // [tok_per_wg * k]
-    float* s_val = (float*)(smem + tok_per_wg * k);   // [tok_per_wg * k]
-    int32_t* s_cursor = smem + 2 * tok_per_wg * k;    // [E]
-
-    const int tid = threadIdx.x;
-    const int wave = tid / WAVE;
-    const int lane = tid % WAVE;
-    const int t0 = blockIdx.x * tok_per_wg;
-    const int ntok = min(tok_per_wg, T - t0);
-
-    for (int e = tid; e < E; e += kRouteThreads) s_cursor[e] = 0;
-
-    for (int i = wave; i < ntok; i += kRouteWaves) {
-        const int t = t0 + i;
-        const float* row = logits + (size_t)t * E;
-        float v[EPL];
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = lane + WAVE * j;
-            v[j] = e < E ? row[e] + 0.0f : 0.0f;   // + 0.0f: -0.0 -> +0.0
-        }
-        uint32_t taken = 0;
-        for (int r = 0; r < k; ++r) {
-            float bv = 0.0f;
-            int be = 0x7fffffff;
-#pragma unroll
-            for (int j = 0; j < EPL; ++j) {
-                const int e = lane + WAVE * j;
-                const bool ok = e < E && !((taken >> j) & 1u);
-                if (ok && (be == 0x7fffffff || v[j] > bv)) {   // ascending e per lane: strict > keeps the lower index
-                    bv = v[j];
-                    be = e;
-                }
-            }
-#pragma unroll
-            for (int off = WAVE / 2; off >= 1; off >>= 1) {
-                const float ov = shfl_xor(bv, off);
-                const int oe = shfl_xor(be, off);
-                const bool o_better = oe != 0x7fffffff &&
-                                      (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-                if (o_better) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            if ((be % WAVE) == lane) taken |= 1u << (be / WAVE);
-            if (lane == 0) {
-                s_exp[i * k + r] = be;
-                s_val[i * k + r] = bv;
-            }
-        }
-    }
-    __syncthreads();
-
-    // softmax over the k chosen logits of each token (max = first chosen)
-    for (int i = wave; i < ntok; i += kRouteWaves) {
-        const float m = s_val[i * k];
-        float part = 0.0f;
-        for (int r = lane; r < k; r += WAVE) part += __expf(s_val[i * k + r] - m);
-#pragma unroll
-        for (int off = WAVE / 2; off >= 1; off >>= 1) part += shfl_xor(part, off);
-        const float inv = 1.0f / part;
-        const int t = t0 + i;
-        for (int r = lane; r < k; r += WAVE) {
-            topk_idx[(size_t)t * k + r] = s_exp[i * k + r];
-            topk_w[(size_t)t * k + r] = __expf(s_val[i * k + r] - m) * inv;
-        }
-    }
-
-    // Stable local ranks and the workgroup histogram: wave 0 walks the
-    // workgroup's assignments in ascending order, 64 at a time.
-    if (wave == 0) {
-        const int n_asg = ntok * k;
-        const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
-        const uint64_t lt = lanemask_lt();
-        for (int base = 0; base < n_asg; base += WAVE) {
-            const int a = base + lane;
-            const bool valid = a < n_asg;
-            const int e = valid ? s_exp[a] : 0;
-            uint64_t match = __ballot(valid);
-            for (int bit = 0; bit < nbits; ++bit) {
-                const bool set = (e >> bit) & 1;
-                const uint64_t bal = __ballot(valid && set);
-                match &= set ? bal : ~bal;
-            }
-            const int rank = __popcll(match & lt);
-            const int cnt = __popcll(match);
-            int prev = 0;
-            if (valid) prev = s_cursor[e];
-            __builtin_amdgcn_wave_barrier();
-            if (valid) {
-                local_rank[(size_t)t0 * k + a] = prev + rank;
-                if (rank == 0) s_cursor[e] = prev + cnt;
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kRouteThreads) wg_hist[(size_t)blockIdx.x * E + e] = s_cursor[e];
+// Order-preserving map of a finite float to uint32 (-0.0 folded onto +0.0).
+__device__ __forceinline__ uint32_t float_key(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kScanThreads = 1024;
+__device__ __forceinline__ int wave_popc_ge(uint32_t key, uint32_t th, bool valid) {
+    return __popcll(__ballot(valid && key >= th));
+}
 
-// Exclusive scan of one value per thread over the workgroup (E <= 1024).
+// Top-k of one token's E logits by one wave.  Lane l holds experts
+// l*EPL .. l*EPL+EPL-1.  s_key/s_e/s_v: this wave's LDS scratch of k entries.
+template <int EPL>
+__device__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* out_idx,
+                           float* out_w, uint32_t* s_key, int* s_e, float* s_v,
+                           int* lds_idx = nullptr) {
+    const int lane = __lane_id();
+    float v[EPL];
+    uint32_t key[EPL];
+    bool ok[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane * EPL + j;
+        ok[j] = e < E;
+        v[j] = ok[j] ? row[e] : 0.0f;
+        key[j] = ok[j] ? float_key(v[j]) : 0u;
+    }
+    // radix select: largest th with count(key >= th) >= k
+    uint32_t th = 0;
+    bool exact = false;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = th | (1u << b);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) c += wave_popc_ge(key[j], cand, ok[j]);
+        if (c >= k) {
+            th = cand;
+            if (c == k) {
+                exact = true;
+                break;
+            }
+        }
+    }
+    // selection mask (per element) and its position in expert order
+    bool sel[EPL];
+    if (exact) {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) sel[j] = ok[j] && key[j] >= th;
+    } else {
+        int gt = 0;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) gt += __popcll(__ballot(ok[j] && key[j] > th));
+        const int need = k - gt;
+        const uint64_t lt = lanemask_lt();
+        int below = 0;   // ties held by lower lanes
+        uint64_t tb[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            tb[j] = __ballot(ok[j] && key[j] == th);
+            below += __popcll(tb[j] & lt);
+        }
+        int own = 0;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const bool tie = ok[j] && key[j] == th;
+            sel[j] = (ok[j] && key[j] > th) || (tie && below + own < need);
+            own += tie ? 1 : 0;
+        }
+    }
+    // compact the k chosen into LDS in expert order
+    {
+        const uint64_t lt = lanemask_lt();
+        int pos = 0;
+        uint64_t sb[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            sb[j] = __ballot(sel[j]);
+            pos += __popcll(sb[j] & lt);
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            if (sel[j]) {
+                s_key[pos] = key[j];
+                s_e[pos] = lane * EPL + j;
+                s_v[pos] = v[j];
+                ++pos;
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // slot of each chosen = number of chosen ahead of it (value desc, index asc);
+    // entries are in ascending expert order, so "index asc" = position order
+    float vmax = -__builtin_huge_valf();
+    for (int p = lane; p < k; p += WAVE) vmax = fmaxf(vmax, s_v[p]);
+#pragma unroll
+    for (int off = WAVE / 2; off >= 1; off >>= 1) vmax = fmaxf(vmax, shfl_xor(vmax, off));
+    float part = 0.0f;
+    for (int p = lane; p < k; p += WAVE) part += __expf(s_v[p] - vmax);
+#pragma unroll
+    for (int off = WAVE / 2; off >= 1; off >>= 1) part += shfl_xor(part, off);
+    const float inv = 1.0f / part;
+    for (int p = lane; p < k; p += WAVE) {
+        const uint32_t kp = s_key[p];
+        int slot = 0;
+        for (int q = 0; q < k; ++q) {
+            const uint32_t kq = s_key[q];
+            slot += (kq > kp || (kq == kp && q < p)) ? 1 : 0;
+        }
+        out_idx[slot] = s_e[p];
+        out_w[slot] = __expf(s_v[p] - vmax) * inv;
+        if (lds_idx) lds_idx[slot] = s_e[p];
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kTopkWaves * WAVE) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+    extern __shared__ uint32_t smem_u[];
+    const int wave = threadIdx.x / WAVE;
+    const int t = blockIdx.x * kTopkWaves + wave;
+    uint32_t* s_key = smem_u + wave * 3 * k;
+    int* s_e = (int*)(s_key + k);
+    float* s_v = (float*)(s_key + 2 * k);
+    if (t < T)
+        topk_token<EPL>(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                        topk_w + (size_t)t * k, s_key, s_e, s_v);
+}
+
+// Expert of each assignment inside a 64-lane chunk -> (rank among equal
+// experts in lower lanes, number of equal experts in the chunk).
+__device__ __forceinline__ void match_rank(int e, bool valid, int nbits, int* rank, int* cnt) {
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t bal = __ballot(valid && set);
+        match &= set ? bal : ~bal;
+    }
+    *rank = __popcll(match & lanemask_lt());
+    *cnt = __popcll(match);
+}
+
+// Exclusive scan of one value per thread over a kGroupThreads workgroup.
 __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     int incl = v;
@@ -146,122 +189,180 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
     if (lane == WAVE - 1) s_wave[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        const int nw = kScanThreads / WAVE;
-        int w = lane < nw ? s_wave[lane] : 0;
+        int w = lane < kGroupWaves ? s_wave[lane] : 0;
         int wi = w;
 #pragma unroll
         for (int off = 1; off < WAVE; off <<= 1) {
             const int o = __shfl_up(wi, off, WAVE);
             if (lane >= off) wi += o;
         }
-        if (lane < nw) s_wave[lane] = wi - w;   // exclusive wave prefix
-        if (lane == nw - 1) s_wave[nw] = wi;    // grand total
+        if (lane < kGroupWaves) s_wave[lane] = wi - w;
+        if (lane == kGroupWaves - 1) s_wave[kGroupWaves] = wi;
     }
     __syncthreads();
     const int res = s_wave[wave] + incl - v;
-    *total = s_wave[kScanThreads / WAVE];
+    *total = s_wave[kGroupWaves];
     __syncthreads();
     return res;
 }
 
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
-    int32_t* __restrict__ wg_hist, int nwg, int E, int block_rows, int max_blocks,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ block_expert, int32_t* __restrict__ block_row,
-    int32_t* __restrict__ n_blocks) {
-    __shared__ int s_wave[kScanThreads / WAVE + 1];
-    const int e = threadIdx.x;
+// Histogram, scan, block map and stable scatter of n = T*k assignments
+// whose experts are eids[0..n).  Needs kGroupThreads threads and
+// kGroupWaves*E + kGroupWaves + 1 ints of LDS at s_hist.
+__device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int max_blocks,
+                          const RoutingDev& r, int* s_hist) {
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    int* s_wave = s_hist + kGroupWaves * E;
+    const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
+    const int seg = (n + kGroupWaves - 1) / kGroupWaves;
+    const int a_begin = min(n, wave * seg), a_end = min(n, a_begin + seg);
+    int* my_hist = s_hist + wave * E;
+
+    for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) s_hist[i] = 0;
+    __syncthreads();
+
+    // pass 1: per-segment histograms
+    for (int base = a_begin; base < a_end; base += WAVE) {
+        const int a = base + lane;
+        const bool valid = a < a_end;
+        const int e = valid ? eids[a] : 0;
+        int rank, cnt;
+        match_rank(e, valid, nbits, &rank, &cnt);
+        if (valid && rank == 0) my_hist[e] += cnt;
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+
+    // per expert: prefix over segments, totals, scans, block map
+    const int e = tid;
     int cnt = 0;
     if (e < E) {
-        // exclusive prefix over workgroups, in place
-        for (int w = 0; w < nwg; ++w) {
-            const int h = wg_hist[(size_t)w * E + e];
-            wg_hist[(size_t)w * E + e] = cnt;
+        for (int w = 0; w < kGroupWaves; ++w) {
+            const int h = s_hist[w * E + e];
+            s_hist[w * E + e] = cnt;
             cnt += h;
         }
     }
-    int total_rows;
+    int total_rows, total_blocks;
     const int off = block_exclusive_scan(e < E ? cnt : 0, s_wave, &total_rows);
     const int nb = e < E ? (cnt + block_rows - 1) / block_rows : 0;
-    int total_blocks;
     const int bstart = block_exclusive_scan(nb, s_wave, &total_blocks);
     if (e < E) {
-        counts[e] = cnt;
-        offsets[e] = off;
+        r.counts[e] = cnt;
+        r.offsets[e] = off;
         for (int i = 0; i < nb; ++i) {
-            block_expert[bstart + i] = e;
-            block_row[bstart + i] = off + block_rows * i;
+            r.block_expert[bstart + i] = e;
+            r.block_row[bstart + i] = off + block_rows * i;
         }
-        for (int w = 0; w < nwg; ++w) wg_hist[(size_t)w * E + e] += off;
+        for (int w = 0; w < kGroupWaves; ++w) s_hist[w * E + e] += off;
     }
     if (e == 0) {
-        offsets[E] = total_rows;
-        n_blocks[0] = total_blocks;
+        r.offsets[E] = total_rows;
+        r.n_blocks[0] = total_blocks;
     }
-    for (int b = total_blocks + e; b < max_blocks; b += kScanThreads) {
-        block_expert[b] = -1;
-        block_row[b] = -1;
+    for (int b = total_blocks + tid; b < max_blocks; b += kGroupThreads) {
+        r.block_expert[b] = -1;
+        r.block_row[b] = -1;
+    }
+    __syncthreads();
+
+    // pass 2: stable scatter
+    for (int base = a_begin; base < a_end; base += WAVE) {
+        const int a = base + lane;
+        const bool valid = a < a_end;
+        const int ea = valid ? eids[a] : 0;
+        int rank, c;
+        match_rank(ea, valid, nbits, &rank, &c);
+        int row = 0;
+        if (valid) row = my_hist[ea] + rank;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            if (rank == 0) my_hist[ea] = row + c;
+            r.sorted_assign[row] = a;
+            r.assign_row[a] = row;
+        }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
-__global__ __launch_bounds__(256) void route_scatter_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ wg_base,
-    const int32_t* __restrict__ local_rank, int n_asg, int E, int asg_per_wg,
-    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_row) {
-    const int a = blockIdx.x * 256 + threadIdx.x;
-    if (a >= n_asg) return;
-    const int e = topk_idx[a];
-    const int w = a / asg_per_wg;
-    const int row = wg_base[(size_t)w * E + e] + local_rank[a];
-    sorted_assign[row] = a;
-    assign_row[a] = row;
+__global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
+    const int32_t* __restrict__ topk_idx, int n, int E, int block_rows, int max_blocks,
+    RoutingDev r) {
+    extern __shared__ int smem_i[];
+    group_all(topk_idx, n, E, block_rows, max_blocks, r, smem_i);
 }
 
-int route_tokens_per_wg(int T, int k) {
-    // keep the per-workgroup assignment list and ranking walk short
-    int tpw = 16;
-    while (tpw > 1 && tpw * k > 4096) tpw >>= 1;
-    (void)T;
-    return tpw;
+// Small T: every wave takes tokens wave, wave+16, ...; experts are kept in
+// LDS for the grouping phase, so the whole routing is one launch.
+template <int EPL>
+__global__ __launch_bounds__(kGroupThreads) void route_fused_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int block_rows, int max_blocks,
+    RoutingDev r) {
+    extern __shared__ int smem_i[];
+    const int wave = threadIdx.x / WAVE;
+    int* s_hist = smem_i;                                  // kGroupWaves*E + kGroupWaves + 1
+    int* s_eids = s_hist + kGroupWaves * E + kGroupWaves + 1;   // T*k
+    uint32_t* s_scr = (uint32_t*)(s_eids + T * k) + wave * 3 * k;
+    for (int t = wave; t < T; t += kGroupWaves) {
+        topk_token<EPL>(logits + (size_t)t * E, E, k, r.topk_idx + (size_t)t * k,
+                        r.topk_w + (size_t)t * k, s_scr, (int*)(s_scr + k),
+                        (float*)(s_scr + 2 * k), s_eids + t * k);
+    }
+    __syncthreads();
+    group_all(s_eids, T * k, E, block_rows, max_blocks, r, s_hist);
 }
 
 size_t route_ws_layout(int T, int E, int k, size_t* off_hist, size_t* off_rank) {
-    const int tpw = route_tokens_per_wg(T, k);
-    const size_t nwg = (size_t)(T + tpw - 1) / tpw;
-    size_t o = 0;
-    *off_hist = o;
-    o += align_up(nwg * E * sizeof(int32_t), 256);
-    *off_rank = o;
-    o += align_up((size_t)T * k * sizeof(int32_t), 256);
-    return o;
+    (void)T;
+    (void)E;
+    (void)k;
+    *off_hist = 0;
+    *off_rank = 0;
+    return 0;   // routing needs no device workspace beyond its outputs
 }
+
+static size_t group_lds_bytes(int E) {
+    return (size_t)(kGroupWaves * E + kGroupWaves + 1) * sizeof(int);
+}
+
+static size_t fused_lds_bytes(int T, int E, int k) {
+    return group_lds_bytes(E) + (size_t)T * k * sizeof(int) +
+           (size_t)kGroupWaves * 3 * k * sizeof(uint32_t);
+}
+
+constexpr size_t kMaxLds = 64 * 1024;
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int block_rows, int max_blocks,
                         const RoutingDev& r, void* ws, hipStream_t stream) {
-    size_t off_hist, off_rank;
-    route_ws_layout(T, E, k, &off_hist, &off_rank);
-    int32_t* wg_hist = (int32_t*)((char*)ws + off_hist);
-    int32_t* local_rank = (int32_t*)((char*)ws + off_rank);
-    const int tpw = route_tokens_per_wg(T, k);
-    const int nwg = (T + tpw - 1) / tpw;
-    const size_t smem = (size_t)(2 * tpw * k + E) * sizeof(int32_t);
+    (void)ws;
     const int epl = (E + WAVE - 1) / WAVE;
-#define MOE_ROUTE_TOPK(N)                                                                     \
-    route_topk_kernel<N><<<nwg, kRouteThreads, smem, stream>>>(logits, T, E, k, tpw,        \
-                                                              r.topk_idx, r.topk_w, wg_hist, \
-                                                              local_rank)
-    if (epl <= 1) MOE_ROUTE_TOPK(1);
-    else if (epl <= 2) MOE_ROUTE_TOPK(2);
-    else if (epl <= 4) MOE_ROUTE_TOPK(4);
-    else if (epl <= 8) MOE_ROUTE_TOPK(8);
-    else MOE_ROUTE_TOPK(16);
-#undef MOE_ROUTE_TOPK
-    route_scan_kernel<<<1, kScanThreads, 0, stream>>>(wg_hist, nwg, E, block_rows, max_blocks,
-                                                      r.counts, r.offsets, r.block_expert,
-                                                      r.block_row, r.n_blocks);
-    const int n_asg = T * k;
-    route_scatter_kernel<<<(n_asg + 255) / 256, 256, 0, stream>>>(
-        r.topk_idx, wg_hist, local_rank, n_asg, E, tpw * k, r.sorted_assign, r.assign_row);
+    const int n = T * k;
+    if (T <= kFusedMaxTokens && fused_lds_bytes(T, E, k) <= kMaxLds) {
+        const size_t smem = fused_lds_bytes(T, E, k);
+#define MOE_FUSED(N)                                                                          \
+    route_fused_kernel<N><<<1, kGroupThreads, smem, stream>>>(logits, T, E, k, block_rows,     \
+                                                             max_blocks, r)
+        if (epl <= 1) MOE_FUSED(1);
+        else if (epl <= 2) MOE_FUSED(2);
+        else if (epl <= 4) MOE_FUSED(4);
+        else if (epl <= 8) MOE_FUSED(8);
+        else MOE_FUSED(16);
+#undef MOE_FUSED
+        return hipGetLastError();
+    }
+    const size_t smem_t = (size_t)kTopkWaves * 3 * k * sizeof(uint32_t);
+    const int grid = (T + kTopkWaves - 1) / kTopkWaves;
+#define MOE_TOPK(N)                                                                         \
+    route_topk_kernel<N><<<grid, kTopkWaves * WAVE, smem_t, stream>>>(logits, T, E, k,     \
+                                                                      r.topk_idx, r.topk_w)
+    if (epl <= 1) MOE_TOPK(1);
+    else if (epl <= 2) MOE_TOPK(2);
+    else if (epl <= 4) MOE_TOPK(4);
+    else if (epl <= 8) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
+    route_group_kernel<<<1, kGroupThreads, group_lds_bytes(E), stream>>>(
+        r.topk_idx, n, E, block_rows, max_blocks, r);
     return hipGetLastError();
 }
 

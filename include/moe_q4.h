@@ -30,7 +30,7 @@
  *     values) is not validated.
  *   - The library holds no mutable global state: calls on different streams
  *     may run concurrently from different threads if their buffers differ.
- *   - Shapes: 1 <= k <= E <= 1024; H, I, I_sh are multiples of 64 (I_sh = 0
+ *   - Shapes: 1 <= k <= E <= 1000; H, I, I_sh are multiples of 64 (I_sh = 0
  *     means no shared expert); T >= 1; T*k*max(H, I) < 2^31;
  *     block_rows is 16, 32 or 64.
  *   - Inputs are finite.  Scales must satisfy |s| < 2^118 (the kernels work
@@ -108,7 +108,8 @@ const char* moe_status_str(int status);
  * block_expert / block_row.  Returns a negative status on bad shapes. */
 int moe_route_max_blocks(int T, int E, int k, int block_rows);
 
-/* Device workspace bytes moe_route needs (0 on bad shapes). */
+/* Device workspace bytes moe_route needs (0 on bad shapes; this build needs
+ * none for valid shapes, and then ws may be NULL). */
 size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows);
 
 /* GPU-resident routing ([P1] "Prefill optimizations", GPU-resident routing

@@ -41,7 +41,7 @@ def test_max_blocks_and_workspace_sizes():
     assert bq.route_max_blocks(1, 256, 8, 32) == 1 + 8
     assert bq.route_max_blocks(64, 16, 2, 32) == 4 + 16
     assert bq.lib().moe_route_max_blocks(1, 256, 8, 48) == bq.MOE_ERR_SHAPE
-    assert bq.route_workspace_bytes(512, 256, 8, 32) > 0
+    assert bq.route_workspace_bytes(512, 256, 8, 32) == 0   # routing needs no workspace
     assert bq.route_workspace_bytes(0, 256, 8, 32) == 0
     # h (T*k x I) + shared h (T x I_sh), bf16
     assert bq.gemm_workspace_bytes(512, 2048, 512, 512, 256, 8, 32) >= 512 * 8 * 512 * 2 + 512 * 512 * 2
@@ -65,16 +65,16 @@ def _mat(codes=FAKE):
 def test_route_rejects_bad_arguments():
     L = bq.lib()
     r = _routing()
-    ok_ws = bq.route_workspace_bytes(64, 16, 2, 32)
+    ok_ws = 256
     assert L.moe_route(None, 64, 16, 2, 32, ctypes.byref(r), FAKE, ok_ws, None) == bq.MOE_ERR_NULL
     assert L.moe_route(FAKE, 64, 16, 2, 32, None, FAKE, ok_ws, None) == bq.MOE_ERR_NULL
     bad = bq.MoeRouting(*([FAKE.value] * 8 + [None]))
     assert L.moe_route(FAKE, 64, 16, 2, 32, ctypes.byref(bad), FAKE, ok_ws, None) == bq.MOE_ERR_NULL
-    for T, E, k, br in [(0, 16, 2, 32), (64, 16, 17, 32), (64, 16, 0, 32), (64, 2000, 2, 32),
+    for T, E, k, br in [(0, 16, 2, 32), (64, 16, 17, 32), (64, 16, 0, 32), (64, 1001, 2, 32),
                         (64, 16, 2, 8), (64, 16, 2, 128)]:
         assert L.moe_route(FAKE, T, E, k, br, ctypes.byref(r), FAKE, 1 << 30, None) == bq.MOE_ERR_SHAPE
-    assert L.moe_route(FAKE, 64, 16, 2, 32, ctypes.byref(r), FAKE, ok_ws - 1, None) == bq.MOE_ERR_WORKSPACE
     assert L.moe_route(P(0x10002), 64, 16, 2, 32, ctypes.byref(r), FAKE, ok_ws, None) == bq.MOE_ERR_ALIGN
+    assert L.moe_route(FAKE, 64, 16, 2, 32, ctypes.byref(r), P(0x10010), ok_ws, None) == bq.MOE_ERR_ALIGN
 
 
 def test_gemm_rejects_bad_arguments():
