@@ -9,23 +9,42 @@
 
 namespace moeq4 {
 
-// One workgroup per token; each thread owns 8 consecutive columns per pass
-// (16-byte loads of every routed row it gathers).
-__global__ __launch_bounds__(256) void combine_kernel(
+// One workgroup per token.  The token's k (row, weight) pairs are staged in
+// LDS once; each thread then owns 8 consecutive columns per pass and issues
+// its k 16-byte row gathers back to back before summing in slot order.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 8;   // gathers in flight per thread
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const uint16_t* __restrict__ expert_out, const uint16_t* __restrict__ shared_out,
     const int32_t* __restrict__ assign_row, const float* __restrict__ topk_w, int H, int k,
     uint16_t* __restrict__ y) {
+    extern __shared__ int s_rw[];   // [k] rows, then [k] weights
+    int* s_row = s_rw;
+    float* s_w = (float*)(s_rw + k);
     const int t = blockIdx.x;
-    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    for (int j = threadIdx.x; j < k; j += kCombineThreads) {
+        s_row[j] = assign_row[(size_t)t * k + j];
+        s_w[j] = topk_w[(size_t)t * k + j];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x * 8; c < H; c += kCombineThreads * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
-            const int row = assign_row[(size_t)t * k + j];
-            const float w = topk_w[(size_t)t * k + j];
-            const u32x4_t v = *(const u32x4_t*)(expert_out + (size_t)row * H + c);
+        for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+            u32x4_t v[kCombineBatch];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = __builtin_fmaf(w, __builtin_bit_cast(float, v[q] << 16), acc[2 * q]);
-                acc[2 * q + 1] = __builtin_fmaf(w, __builtin_bit_cast(float, v[q] & 0xFFFF0000u), acc[2 * q + 1]);
+            for (int j = 0; j < kCombineBatch; ++j)
+                if (j0 + j < k) v[j] = *(const u32x4_t*)(expert_out + (size_t)s_row[j0 + j] * H + c);
+#pragma unroll
+            for (int j = 0; j < kCombineBatch; ++j) {
+                if (j0 + j >= k) break;
+                const float w = s_w[j0 + j];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = __builtin_fmaf(w, __builtin_bit_cast(float, v[j][q] << 16), acc[2 * q]);
+                    acc[2 * q + 1] =
+                        __builtin_fmaf(w, __builtin_bit_cast(float, v[j][q] & 0xFFFF0000u), acc[2 * q + 1]);
+                }
             }
         }
         if (shared_out) {
@@ -46,7 +65,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_combine(const uint16_t* expert_out, const uint16_t* shared_out,
                           const int32_t* assign_row, const float* topk_w, int T, int H, int k,
                           uint16_t* y, hipStream_t stream) {
-    combine_kernel<<<T, 256, 0, stream>>>(expert_out, shared_out, assign_row, topk_w, H, k, y);
+    combine_kernel<<<T, kCombineThreads, (size_t)2 * k * sizeof(int), stream>>>(
+        expert_out, shared_out, assign_row, topk_w, H, k, y);
     return hipGetLastError();
 }
 

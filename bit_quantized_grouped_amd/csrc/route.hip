@@ -221,15 +221,27 @@ __device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int
     for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) s_hist[i] = 0;
     __syncthreads();
 
-    // pass 1: per-segment histograms
-    for (int base = a_begin; base < a_end; base += WAVE) {
-        const int a = base + lane;
-        const bool valid = a < a_end;
-        const int e = valid ? eids[a] : 0;
-        int rank, cnt;
-        match_rank(e, valid, nbits, &rank, &cnt);
-        if (valid && rank == 0) my_hist[e] += cnt;
-        __builtin_amdgcn_wave_barrier();
+    // pass 1: per-segment histograms.  The segment is walked 64 assignments
+    // at a time; up to kPre chunks of expert ids are fetched ahead into
+    // registers so one memory latency covers kPre chunks.
+    constexpr int kPre = 16;
+    for (int sb = a_begin; sb < a_end; sb += kPre * WAVE) {
+        int ids[kPre];
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int a = sb + q * WAVE + lane;
+            ids[q] = a < a_end ? eids[a] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int base = sb + q * WAVE;
+            if (base >= a_end) break;
+            const bool valid = base + lane < a_end;
+            int rank, cnt;
+            match_rank(ids[q], valid, nbits, &rank, &cnt);
+            if (valid && rank == 0) my_hist[ids[q]] += cnt;
+            __builtin_amdgcn_wave_barrier();
+        }
     }
     __syncthreads();
 
@@ -266,22 +278,33 @@ __device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int
     }
     __syncthreads();
 
-    // pass 2: stable scatter
-    for (int base = a_begin; base < a_end; base += WAVE) {
-        const int a = base + lane;
-        const bool valid = a < a_end;
-        const int ea = valid ? eids[a] : 0;
-        int rank, c;
-        match_rank(ea, valid, nbits, &rank, &c);
-        int row = 0;
-        if (valid) row = my_hist[ea] + rank;
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-            if (rank == 0) my_hist[ea] = row + c;
-            r.sorted_assign[row] = a;
-            r.assign_row[a] = row;
+    // pass 2: stable scatter (same walk; ranks continue from the segment bases)
+    for (int sb = a_begin; sb < a_end; sb += kPre * WAVE) {
+        int ids[kPre];
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int a = sb + q * WAVE + lane;
+            ids[q] = a < a_end ? eids[a] : 0;
         }
-        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int base = sb + q * WAVE;
+            if (base >= a_end) break;
+            const int a = base + lane;
+            const bool valid = a < a_end;
+            const int ea = ids[q];
+            int rank, c;
+            match_rank(ea, valid, nbits, &rank, &c);
+            int row = 0;
+            if (valid) row = my_hist[ea] + rank;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                if (rank == 0) my_hist[ea] = row + c;
+                r.sorted_assign[row] = a;
+                r.assign_row[a] = row;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
     }
 }
 
