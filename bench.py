@@ -2,14 +2,19 @@
 
 One step = one full layer call (moe_route -> moe_grouped_gemm_q4 ->
 moe_combine) over the 512-token prefill workload (H 2048, I 512, 256 experts
-top-8 + 1 shared expert, 4-bit g64 weights), inputs resident in HBM.
-Prints ONE JSON line.  Secondary workloads (2048-token prefill, batch-1
-decode over 1000 tokens, skewed 8192-token prefill in chunks of 2048) are
-timed too and reported under "extra".
+top-8 + 1 shared expert of I 512, 4-bit g64 weights), inputs resident in HBM.
+Prints ONE JSON line.  The 2048-token prefill, batch-1 decode over 1000
+tokens and the skewed 8192-token prefill in chunks of 2048 are timed too and
+reported under "extra".
+
+--calibrate-copy MB runs only a plain device-to-device copy of MB megabytes
+(five times); rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE over it gives the
+scale between those counters and true bytes.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,16 +27,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 MFMA
-EXPERT_BYTES_PER_WEIGHT = 0.5 + 4.0 / 64   # code nibble + bf16 scale and bias per 64
+BYTES_PER_WEIGHT = 0.5 + 4.0 / 64   # code nibble + bf16 scale and bias per 64 weights
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_prefill512.txt")
+KERNEL_SRC = os.path.join(ROOT, "bit_quantized_grouped_amd", "csrc", "gemm_q4.hip")
 
 
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
-
-
-def expert_bytes(H, I):
-    return int(3 * H * I * EXPERT_BYTES_PER_WEIGHT)
 
 
 def layer_flops(T, H, I, k, I_sh):
@@ -47,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
     return ap.parse_args()
 
 
@@ -64,6 +68,35 @@ def timed(fn, steps, warmup, torch):
     return s.elapsed_time(e) / steps   # ms per call
 
 
+def kernel_src_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(ln.strip().split("=", 1) for ln in f if "=" in ln and not ln.startswith("#"))
+        if kv.get("kernel_src_sha") != kernel_src_sha():
+            return None
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mb, torch):
+    n = mb * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -72,6 +105,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, torch)
+        return
     import bit_quantized_grouped_amd as bq
     from workload import CONFIGS, make_activations, make_weights
 
@@ -82,6 +118,7 @@ def main():
     w = make_weights(cfg, seed=0)
     layer = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
     log("weights resident")
+    br = layer.block_rows
 
     def prep(c):
         xb, lg = make_activations(c)
@@ -90,40 +127,41 @@ def main():
     # ---------------- headline: prefill 512 ----------------
     x, lg = prep(cfg)
     T = cfg.T
-    step = lambda: layer.forward(x, lg)  # noqa: E731
-    ms = timed(step, args.steps, args.warmup, torch)
+    ms = timed(lambda: layer.forward(x, lg), args.steps, args.warmup, torch)
     bufs = layer.buffers(T)
     counts = bufs["routing"].counts.cpu().numpy()
     touched = int(np.count_nonzero(counts))
 
-    # per-call durations (events on the launch stream around each ABI call)
+    # per-phase durations: events on the launch stream around each ABI call
     r, ws_r, ws_g = bufs["routing"], bufs["route_ws"], bufs["gemm_ws"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.warmup):
-        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         ev = evs[i]
         ev[0].record()
-        bq.moe_route(lg, cfg.k, layer.block_rows, r, ws_r)
+        bq.moe_route(lg, cfg.k, br, r, ws_r)
         ev[1].record()
-        bq.moe_grouped_gemm_q4(x, cfg.I, cfg.I_sh, cfg.E, cfg.k, layer.block_rows, r,
-                               *layer.weight_mats(), bufs["expert_out"], bufs["shared_out"], ws_g)
+        bq.moe_expert_gateup_q4(x, cfg.I, cfg.I_sh, cfg.E, cfg.k, br, r, layer.gate, layer.up,
+                                layer.sh_gate, layer.sh_up, ws_g)
         ev[2].record()
-        bq.moe_combine(bufs["expert_out"], bufs["shared_out"], r, cfg.k, bufs["y"])
+        bq.moe_expert_down_q4(T, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, br, r, layer.down,
+                              layer.sh_down, bufs["expert_out"], bufs["shared_out"], ws_g)
         ev[3].record()
+        bq.moe_combine(bufs["expert_out"], bufs["shared_out"], r, cfg.k, bufs["y"])
+        ev[4].record()
     torch.cuda.synchronize()
-    t_route = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs])) * 1e-3
-    t_gemm = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in evs])) * 1e-3
-    t_comb = float(np.mean([ev[2].elapsed_time(ev[3]) for ev in evs])) * 1e-3
+    phase = [float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs])) * 1e-3 for j in range(4)]
+    t_route, t_gu, t_dn, t_comb = phase
 
-    eb = expert_bytes(cfg.H, cfg.I)
-    gemm_bytes = (touched + 1) * eb + T * cfg.H * 2
-    layer_bytes = (touched + 1) * eb + T * cfg.H * 2 + T * cfg.E * 4 + T * cfg.H * 2
+    # algorithmic bytes: packed weights of touched experts + shared expert, x in, logits in, y out
+    gu_bytes_per_expert = int(2 * cfg.I * cfg.H * BYTES_PER_WEIGHT)
+    expert_bytes = int(3 * cfg.I * cfg.H * BYTES_PER_WEIGHT)
+    gu_bytes = (touched + 1) * gu_bytes_per_expert + T * cfg.H * 2
+    layer_bytes = (touched + 1) * expert_bytes + T * cfg.H * 2 + T * cfg.E * 4 + T * cfg.H * 2
     flops = layer_flops(T, cfg.H, cfg.I, cfg.k, cfg.I_sh)
     t_layer = ms * 1e-3
     t_roof = max(flops / MFMA_BF16_PEAK, layer_bytes / HBM_PEAK)
-    achieved = gemm_bytes / t_gemm
+    achieved = gu_bytes / t_gu
     result = {
         "metric": "MoE-layer tokens/s (prefill 512 tokens, 256 experts top-8 + shared, 4-bit g64)",
         "value": T / t_layer,
@@ -138,20 +176,22 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "prefill512", "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
-                   "k": cfg.k, "I_shared": cfg.I_sh, "block_rows": layer.block_rows,
-                   "weights": "4-bit codes, bf16 scale+bias per 64"},
-        "roofline": {"bound": "hbm", "kernel": "moe_grouped_gemm_q4 (gate/up+SwiGLU and down kernels)",
+                   "k": cfg.k, "I_shared": cfg.I_sh, "block_rows": br,
+                   "weights": "4-bit codes, bf16 scale+bias per 64 along K"},
+        "roofline": {"bound": "hbm", "kernel": "grouped_q4_kernel gate/up+SwiGLU (moe_expert_gateup_q4)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": None,
-                     "algorithmic_bytes": gemm_bytes, "avg_launch_us": t_gemm * 1e6},
-        "layer": {"route_us": t_route * 1e6, "gemm_us": t_gemm * 1e6, "combine_us": t_comb * 1e6,
-                  "touched_experts": touched, "layer_bytes": layer_bytes, "layer_flops": flops,
+                     "frac": achieved / HBM_PEAK, "traffic": read_traffic(),
+                     "algorithmic_bytes": gu_bytes, "avg_launch_us": t_gu * 1e6},
+        "layer": {"route_us": t_route * 1e6, "gateup_us": t_gu * 1e6, "down_us": t_dn * 1e6,
+                  "combine_us": t_comb * 1e6, "touched_experts": touched,
+                  "algorithmic_bytes": layer_bytes, "algorithmic_flops": flops,
                   "roofline_frac": t_roof / t_layer,
                   "mfma_frac": flops / t_layer / MFMA_BF16_PEAK,
                   "hbm_frac": layer_bytes / t_layer / HBM_PEAK},
     }
-    log(f"prefill512: {ms*1e3:.1f} us/call, {T/t_layer:,.0f} tok/s, gemm {t_gemm*1e6:.1f} us "
-        f"({achieved/1e9:.0f} GB/s), route {t_route*1e6:.1f} us, combine {t_comb*1e6:.1f} us")
+    log(f"prefill512: {ms*1e3:.1f} us/call, {T/t_layer:,.0f} tok/s | route {t_route*1e6:.1f} "
+        f"gateup {t_gu*1e6:.1f} ({achieved/1e9:.0f} GB/s) down {t_dn*1e6:.1f} "
+        f"combine {t_comb*1e6:.1f} us")
 
     # ---------------- secondary workloads ----------------
     extra = {}
@@ -164,10 +204,11 @@ def main():
             cnt = layer.buffers(c.T)["routing"].counts.cpu().numpy()
             tch = int(np.count_nonzero(cnt))
             fl = layer_flops(c.T, c.H, c.I, c.k, c.I_sh)
-            by = (tch + 1) * eb + c.T * c.H * 4 + c.T * c.E * 4
+            by = (tch + 1) * expert_bytes + c.T * c.H * 4 + c.T * c.E * 4
             t = ms2 * 1e-3
             extra["prefill2048"] = {"tokens_per_s": c.T / t, "us_per_call": ms2 * 1e3,
                                     "mfma_frac": fl / t / MFMA_BF16_PEAK,
+                                    "hbm_frac": by / t / HBM_PEAK,
                                     "roofline_frac": max(fl / MFMA_BF16_PEAK, by / HBM_PEAK) / t}
             log(f"prefill2048: {ms2*1e3:.1f} us/call, {c.T/t:,.0f} tok/s, "
                 f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%")
@@ -184,9 +225,10 @@ def main():
 
             msd = timed(run_tokens, 3, 1, torch)       # ms per 1000 tokens
             t_tok = msd * 1e-3 / c.T
-            by_tok = 9 * eb + c.H * 4 + c.E * 4
+            by_tok = 9 * expert_bytes + c.H * 4 + c.E * 4
             extra["decode"] = {"tokens_per_s": 1.0 / t_tok, "us_per_token": t_tok * 1e6,
                                "hbm_frac": by_tok / t_tok / HBM_PEAK,
+                               "path": "three calls per token (route, grouped GEMM, combine)",
                                "note": "1000 single-token calls back to back, same layer (warm caches)"}
             log(f"decode: {t_tok*1e6:.2f} us/token, HBM {100*by_tok/t_tok/HBM_PEAK:.1f}%")
         if not only or "skew8192" in only:

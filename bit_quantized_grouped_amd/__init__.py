@@ -55,6 +55,10 @@ _SIGNATURES = {
     "moe_gemm_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_grouped_gemm_q4": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
                             + [ctypes.POINTER(MoeQ4Mat)] * 6 + [_P, _P, _P, _S, _P]),
+    "moe_expert_gateup_q4": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
+                             + [ctypes.POINTER(MoeQ4Mat)] * 4 + [_P, _S, _P]),
+    "moe_expert_down_q4": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
+                           + [ctypes.POINTER(MoeQ4Mat)] * 2 + [_P, _P, _P, _S, _P]),
     "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
     "moe_layer_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_layer_chunked": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I]
@@ -192,6 +196,25 @@ def moe_grouped_gemm_q4(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, bloc
         _mat(gate), _mat(up), _mat(down), _mat(sh_gate), _mat(sh_up), _mat(sh_down),
         _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, x.device)), "moe_grouped_gemm_q4")
+
+
+def moe_expert_gateup_q4(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, block_rows: int,
+                         routing: DeviceRouting, gate, up, sh_gate, sh_up, ws: torch.Tensor,
+                         stream=None):
+    T, H = x.shape
+    _check(lib().moe_expert_gateup_q4(
+        _ptr(x), T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct),
+        _mat(gate), _mat(up), _mat(sh_gate), _mat(sh_up), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream, x.device)), "moe_expert_gateup_q4")
+
+
+def moe_expert_down_q4(T: int, H: int, I: int, I_sh: int, E: int, k: int, block_rows: int,
+                       routing: DeviceRouting, down, sh_down, expert_out: torch.Tensor, shared_out,
+                       ws: torch.Tensor, stream=None):
+    _check(lib().moe_expert_down_q4(
+        T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct), _mat(down), _mat(sh_down),
+        _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream, expert_out.device)), "moe_expert_down_q4")
 
 
 def moe_combine(expert_out: torch.Tensor, shared_out, routing: DeviceRouting, k: int,

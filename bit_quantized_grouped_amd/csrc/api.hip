@@ -178,6 +178,41 @@ size_t moe_gemm_workspace_bytes(int T, int H, int I, int I_sh, int E, int k, int
     return gemm_ws_layout(T, I, I_sh, k, &a, &b);
 }
 
+static GemmProblem make_problem(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
+                                int block_rows, const moe_routing* r, const moe_q4_mat* gate,
+                                const moe_q4_mat* up, const moe_q4_mat* down,
+                                const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                                const moe_q4_mat* sh_down, uint16_t* expert_out,
+                                uint16_t* shared_out) {
+    GemmProblem p{};
+    p.x = x;
+    p.T = T;
+    p.H = H;
+    p.I = I;
+    p.I_sh = I_sh;
+    p.E = E;
+    p.k = k;
+    p.block_rows = block_rows;
+    p.max_blocks = max_blocks_of(T, E, k, block_rows);
+    p.r = to_dev(r);
+    p.gate = to_dev(gate);
+    p.up = to_dev(up);
+    p.down = to_dev(down);
+    p.sh_gate = to_dev(sh_gate);
+    p.sh_up = to_dev(sh_up);
+    p.sh_down = to_dev(sh_down);
+    p.expert_out = expert_out;
+    p.shared_out = shared_out;
+    return p;
+}
+
+static int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (!ws) return MOE_ERR_NULL;
+    if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
 int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
                         int block_rows, const moe_routing* r, const moe_q4_mat* gate,
                         const moe_q4_mat* up, const moe_q4_mat* down, const moe_q4_mat* sh_gate,
@@ -187,31 +222,69 @@ int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E,
         int st = gemm_args_ok(x, T, H, I, I_sh, E, k, block_rows, r, gate, up, down, sh_gate,
                               sh_up, sh_down, expert_out, shared_out);
         if (st) return st;
-        if (!ws) return MOE_ERR_NULL;
-        if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
-        if (ws_bytes < moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))
-            return MOE_ERR_WORKSPACE;
-        GemmProblem p{};
-        p.x = x;
-        p.T = T;
-        p.H = H;
-        p.I = I;
-        p.I_sh = I_sh;
-        p.E = E;
-        p.k = k;
-        p.block_rows = block_rows;
-        p.max_blocks = max_blocks_of(T, E, k, block_rows);
-        p.r = to_dev(r);
-        p.gate = to_dev(gate);
-        p.up = to_dev(up);
-        p.down = to_dev(down);
-        p.sh_gate = to_dev(sh_gate);
-        p.sh_up = to_dev(sh_up);
-        p.sh_down = to_dev(sh_down);
-        p.expert_out = expert_out;
-        p.shared_out = shared_out;
-        const hipError_t e = launch_grouped_gemm(p, ws, stream);
+        if ((st = check_ws(ws, ws_bytes, moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))))
+            return st;
+        const GemmProblem p = make_problem(x, T, H, I, I_sh, E, k, block_rows, r, gate, up, down,
+                                           sh_gate, sh_up, sh_down, expert_out, shared_out);
+        hipError_t e = launch_gateup(p, ws, stream);
+        if (e == hipSuccess) e = launch_down(p, ws, stream);
         return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_expert_gateup_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
+                         int block_rows, const moe_routing* r, const moe_q4_mat* gate,
+                         const moe_q4_mat* up, const moe_q4_mat* sh_gate,
+                         const moe_q4_mat* sh_up, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    try {
+        int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
+        if (st) return st;
+        if (!x) return MOE_ERR_NULL;
+        if ((st = check_routing(r))) return st;
+        if ((st = check_mat(gate)) || (st = check_mat(up))) return st;
+        if (I_sh) {
+            if ((st = check_mat(sh_gate)) || (st = check_mat(sh_up))) return st;
+        } else if (sh_gate || sh_up) {
+            return MOE_ERR_SHAPE;
+        }
+        if (!aligned(x, 16)) return MOE_ERR_ALIGN;
+        if ((st = check_ws(ws, ws_bytes, moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))))
+            return st;
+        const GemmProblem p = make_problem(x, T, H, I, I_sh, E, k, block_rows, r, gate, up,
+                                           nullptr, sh_gate, sh_up, nullptr, nullptr, nullptr);
+        return launch_gateup(p, ws, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_expert_down_q4(int T, int H, int I, int I_sh, int E, int k, int block_rows,
+                       const moe_routing* r, const moe_q4_mat* down, const moe_q4_mat* sh_down,
+                       uint16_t* expert_out, uint16_t* shared_out, const void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    try {
+        int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
+        if (st) return st;
+        if (!expert_out) return MOE_ERR_NULL;
+        if ((st = check_routing(r))) return st;
+        if ((st = check_mat(down))) return st;
+        if (I_sh) {
+            if (!shared_out) return MOE_ERR_NULL;
+            if ((st = check_mat(sh_down))) return st;
+            if (!aligned(shared_out, 16)) return MOE_ERR_ALIGN;
+        } else if (sh_down || shared_out) {
+            return MOE_ERR_SHAPE;
+        }
+        if (!aligned(expert_out, 16)) return MOE_ERR_ALIGN;
+        if ((st = check_ws(ws, ws_bytes, moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))))
+            return st;
+        const GemmProblem p = make_problem(nullptr, T, H, I, I_sh, E, k, block_rows, r, nullptr,
+                                           nullptr, down, nullptr, nullptr, sh_down, expert_out,
+                                           shared_out);
+        return launch_down(p, ws, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     } catch (...) {
         return MOE_ERR_HIP;
     }

@@ -440,14 +440,7 @@ static void launch_grouped(GroupedArgs a, int mt, int kc, int n_max, int slots, 
     else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES>(a, kc, grid, G, wg_per_cu, stream);
 }
 
-hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t stream) {
-    size_t off_h, off_hsh;
-    gemm_ws_layout(p.T, p.I, p.I_sh, p.k, &off_h, &off_hsh);
-    uint16_t* h = (uint16_t*)((char*)ws + off_h);
-    uint16_t* h_sh = (uint16_t*)((char*)ws + off_hsh);
-    const int mt = p.block_rows;
-    const int sh_blocks = p.I_sh ? (p.T + mt - 1) / mt : 0;
-
+static GroupedArgs common_args(const GemmProblem& p) {
     GroupedArgs a{};
     a.k = p.k;
     a.T = p.T;
@@ -456,10 +449,16 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t strea
     a.block_row = p.r.block_row;
     a.n_blocks = p.r.n_blocks;
     a.offsets = p.r.offsets;
-    a.sh_blocks = sh_blocks;
-    const int slots = sh_blocks + p.max_blocks;
+    a.sh_blocks = p.I_sh ? (p.T + p.block_rows - 1) / p.block_rows : 0;
+    return a;
+}
 
-    // gate + up with SwiGLU: A = x (gathered), N = I, K = H
+// gate + up with SwiGLU: A = x (gathered by token), N = I, K = H -> h in ws
+hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
+    size_t off_h, off_hsh;
+    gemm_ws_layout(p.T, p.I, p.I_sh, p.k, &off_h, &off_hsh);
+    GroupedArgs a = common_args(p);
+    const int slots = a.sh_blocks + p.max_blocks;
     a.a_routed = p.x;
     a.a_shared = p.x;
     a.lda_routed = a.lda_shared = p.H;
@@ -473,15 +472,22 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t strea
     a.K = p.H;
     a.N_sh = p.I_sh;
     a.K_sh = p.H;
-    a.out_routed = h;
-    a.out_shared = h_sh;
+    a.out_routed = (uint16_t*)((char*)ws + off_h);
+    a.out_shared = (uint16_t*)((char*)ws + off_hsh);
     launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES>(
-        a, mt, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh, slots, p.H / 64,
+        a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh, slots, p.H / 64,
         MOE_GU_WG_PER_CU, stream);
+    return hipGetLastError();
+}
 
-    // down: A = h rows (contiguous), N = H, K = I
-    a.a_routed = h;
-    a.a_shared = h_sh;
+// down: A = h rows (contiguous, from ws), N = H, K = I -> expert_out / shared_out
+hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream) {
+    size_t off_h, off_hsh;
+    gemm_ws_layout(p.T, p.I, p.I_sh, p.k, &off_h, &off_hsh);
+    GroupedArgs a = common_args(p);
+    const int slots = a.sh_blocks + p.max_blocks;
+    a.a_routed = (const uint16_t*)((const char*)ws + off_h);
+    a.a_shared = (const uint16_t*)((const char*)ws + off_hsh);
     a.lda_routed = p.I;
     a.lda_shared = p.I_sh;
     a.rows_routed = p.T * p.k;
@@ -496,7 +502,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t strea
     a.out_routed = p.expert_out;
     a.out_shared = p.shared_out;
     launch_grouped<1, MOE_DN_NSUB, MOE_DN_DEPTH, MOE_DN_WAVES>(
-        a, mt, pick_kc(p.I, p.I_sh, MOE_DN_KC), p.H, slots,
+        a, p.block_rows, pick_kc(p.I, p.I_sh, MOE_DN_KC), p.H, slots,
         (p.I > p.I_sh ? p.I : p.I_sh) / 64, MOE_DN_WG_PER_CU, stream);
     return hipGetLastError();
 }

@@ -44,7 +44,8 @@ struct GemmProblem {
     uint16_t* shared_out;
 };
 size_t gemm_ws_layout(int T, int I, int I_sh, int k, size_t* off_h, size_t* off_hsh);
-hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, hipStream_t stream);
+hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream);
+hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream);
 
 // combine.hip
 hipError_t launch_combine(const uint16_t* expert_out, const uint16_t* shared_out,

@@ -145,6 +145,28 @@ int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E,
                         uint16_t* expert_out, uint16_t* shared_out,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The two phases of moe_grouped_gemm_q4, for callers that schedule or time
+ * them separately.  They share the workspace layout of moe_grouped_gemm_q4:
+ * moe_expert_gateup_q4 writes the bf16 SwiGLU activations h (routed rows in
+ * sorted-row order, then the shared expert's rows) into ws, and
+ * moe_expert_down_q4 reads them from the same ws.  Calling both in order on
+ * one stream equals moe_grouped_gemm_q4.
+ *   gateup: h = bf16(silu(x Wg^T) * (x Wu^T)) per routed row and per token
+ *           for the shared expert ([P1] "Prefill optimizations"; [P3]);
+ *   down:   expert_out / shared_out = bf16(h Wd^T).
+ * Arguments and status codes as for moe_grouped_gemm_q4; sh_gate/sh_up/sh_down
+ * and shared_out are NULL iff I_sh == 0. */
+int moe_expert_gateup_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
+                         int block_rows, const moe_routing* r,
+                         const moe_q4_mat* gate, const moe_q4_mat* up,
+                         const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+int moe_expert_down_q4(int T, int H, int I, int I_sh, int E, int k, int block_rows,
+                       const moe_routing* r, const moe_q4_mat* down, const moe_q4_mat* sh_down,
+                       uint16_t* expert_out, uint16_t* shared_out,
+                       const void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Weighted combine: y[t] = sum_j topk_w[t,j] * expert_out[assign_row[t*k+j]]
  * + shared_out[t], summed in fp32 in slot order with the shared expert last
  * (weight 1; the pages name no shared-expert gate), rounded once to bf16.

@@ -117,3 +117,27 @@ def test_combine_and_chunked_reject_bad_arguments():
     args = lambda chunk, wsb: [FAKE, FAKE, 64, 256, 128, 128, 16, 2, 32, chunk] + mats + [FAKE, FAKE, wsb, None]  # noqa: E731
     assert L.moe_layer_chunked(*args(0, ws)) == bq.MOE_ERR_SHAPE
     assert L.moe_layer_chunked(*args(32, ws - 1)) == bq.MOE_ERR_WORKSPACE
+
+
+def test_split_phases_reject_bad_arguments():
+    L = bq.lib()
+    r = _routing()
+    m = _mat()
+    ws = bq.gemm_workspace_bytes(64, 256, 128, 128, 16, 2, 32)
+    gu = lambda x=FAKE, I_sh=128, mats=None, wsb=ws, wsp=FAKE: L.moe_expert_gateup_q4(  # noqa: E731
+        x, 64, 256, 128, I_sh, 16, 2, 32, ctypes.byref(r),
+        *[ctypes.byref(q) if q is not None else None for q in (mats or [m] * 4)], wsp, wsb, None)
+    assert gu(x=None) == bq.MOE_ERR_NULL
+    assert gu(x=P(0x10002)) == bq.MOE_ERR_ALIGN
+    assert gu(I_sh=0) == bq.MOE_ERR_SHAPE                     # shared matrices without I_sh
+    assert gu(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
+    assert gu(wsp=None) == bq.MOE_ERR_NULL
+    assert gu(wsp=P(0x10010)) == bq.MOE_ERR_ALIGN
+    dn = lambda eo=FAKE, so=FAKE, I_sh=128, mats=None, wsb=ws: L.moe_expert_down_q4(  # noqa: E731
+        64, 256, 128, I_sh, 16, 2, 32, ctypes.byref(r),
+        *[ctypes.byref(q) if q is not None else None for q in (mats or [m] * 2)], eo, so, FAKE, wsb, None)
+    assert dn(eo=None) == bq.MOE_ERR_NULL
+    assert dn(so=None) == bq.MOE_ERR_NULL
+    assert dn(eo=MISALIGNED) == bq.MOE_ERR_ALIGN
+    assert dn(mats=[_mat(MISALIGNED), m]) == bq.MOE_ERR_ALIGN
+    assert dn(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE

@@ -197,3 +197,23 @@ def test_skewed_chunked_workload(big_layer):
         # the tolerance normaliser is the chunk's max|y|; the sample's max is a lower bound,
         # so this check is at least as strict
         assert_close_layer(y_bits[s], ref["y"], what=f"chunk {c0}")
+
+
+def test_split_phases_equal_grouped_gemm():
+    cfg = small_config(150, 512, 256, 32, 4, 256, seed=31)
+    w = make_weights(cfg, seed=9, cache=False)
+    x_bits, logits = make_activations(cfg)
+    layer = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
+    announce("split gateup/down vs grouped gemm")
+    got = run_layer(layer, x_bits, logits)
+    b = layer.buffers(cfg.T)
+    eo = torch.empty_like(b["expert_out"])
+    so = torch.empty_like(b["shared_out"])
+    x = bq.bf16_from_bits(x_bits, DEV)
+    bq.moe_expert_gateup_q4(x, cfg.I, cfg.I_sh, cfg.E, cfg.k, 32, b["routing"], layer.gate, layer.up,
+                            layer.sh_gate, layer.sh_up, b["gemm_ws"])
+    bq.moe_expert_down_q4(cfg.T, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, 32, b["routing"], layer.down,
+                          layer.sh_down, eo, so, b["gemm_ws"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bq.bf16_to_bits(eo), got["expert_out"])
+    assert np.array_equal(bq.bf16_to_bits(so), got["shared_out"])
