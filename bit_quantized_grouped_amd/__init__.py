@@ -60,6 +60,11 @@ _SIGNATURES = {
     "moe_expert_down_q4": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
                            + [ctypes.POINTER(MoeQ4Mat)] * 2 + [_P, _P, _P, _S, _P]),
     "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
+    "moe_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "moe_decode_q4": (_I, [_P, _P, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(MoeQ4Mat)] * 6
+                      + [ctypes.POINTER(MoeRouting), _P, _P, _S, _P]),
+    "moe_decode_q4_sequential": (_I, [_P, _P, _I, _I, _I, _I, _I, _I]
+                                 + [ctypes.POINTER(MoeQ4Mat)] * 6 + [_P, _P, _S, _P]),
     "moe_layer_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_layer_chunked": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I]
                           + [ctypes.POINTER(MoeQ4Mat)] * 6 + [_P, _P, _S, _P]),
@@ -224,6 +229,35 @@ def moe_combine(expert_out: torch.Tensor, shared_out, routing: DeviceRouting, k:
                              T, H, k, _ptr(y), _stream(stream, y.device)), "moe_combine")
 
 
+def decode_workspace_bytes(H, I, I_sh, E, k) -> int:
+    return lib().moe_decode_workspace_bytes(H, I, I_sh, E, k)
+
+
+def moe_decode_q4(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
+                  block_rows: int, gate, up, down, sh_gate, sh_up, sh_down, routing, y: torch.Tensor,
+                  ws: torch.Tensor, stream=None):
+    """One token (x [1, H], logits [1, E]) through the whole layer in one launch."""
+    H = x.shape[1]
+    E = logits.shape[1]
+    _check(lib().moe_decode_q4(
+        _ptr(x), _ptr(logits), H, I, I_sh, E, k, block_rows, _mat(gate), _mat(up), _mat(down),
+        _mat(sh_gate), _mat(sh_up), _mat(sh_down),
+        None if routing is None else ctypes.byref(routing.struct), _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream, x.device)), "moe_decode_q4")
+
+
+def moe_decode_q4_sequential(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
+                             gate, up, down, sh_gate, sh_up, sh_down, y: torch.Tensor,
+                             ws: torch.Tensor, stream=None):
+    """x [n, H], logits [n, E]: n single-token decode launches back to back."""
+    n, H = x.shape
+    E = logits.shape[1]
+    _check(lib().moe_decode_q4_sequential(
+        _ptr(x), _ptr(logits), n, H, I, I_sh, E, k, _mat(gate), _mat(up), _mat(down),
+        _mat(sh_gate), _mat(sh_up), _mat(sh_down), _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream, x.device)), "moe_decode_q4_sequential")
+
+
 def moe_layer_chunked(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
                       block_rows: int, chunk_tokens: int, gate, up, down, sh_gate, sh_up,
                       sh_down, y: torch.Tensor, ws: torch.Tensor, stream=None):
@@ -289,6 +323,16 @@ class MoeLayer:
                             stream)
         moe_combine(b["expert_out"], b["shared_out"], b["routing"], self.k, y, stream)
         return dict(b, y=y)
+
+    def decode(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, routing=None,
+               ws=None, stream=None):
+        """One token through the fused single-launch decode path; returns the workspace."""
+        if ws is None:
+            ws = _bytes_tensor(decode_workspace_bytes(self.H, self.I, self.I_sh, self.E, self.k),
+                               self.device)
+        moe_decode_q4(x, logits, self.I, self.I_sh, self.k, self.block_rows, *self.weight_mats(),
+                      routing, y, ws, stream)
+        return ws
 
     def forward_chunked(self, x, logits, chunk_tokens: int, y: torch.Tensor, ws=None, stream=None):
         T = x.shape[0]

@@ -306,6 +306,73 @@ int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const mo
     }
 }
 
+size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k) {
+    if (check_layer_shape(1, H, I, I_sh, E, k, 32) || k > 64) return 0;
+    return decode_ws_bytes(I, I_sh, k);
+}
+
+int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh, int E, int k,
+                  int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
+                  const moe_q4_mat* down, const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                  const moe_q4_mat* sh_down, const moe_routing* r, uint16_t* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+    try {
+        int st = check_layer_shape(1, H, I, I_sh, E, k, block_rows);
+        if (st) return st;
+        if (k > 64) return MOE_ERR_SHAPE;
+        if (!x || !logits || !y) return MOE_ERR_NULL;
+        if ((st = check_mat(gate)) || (st = check_mat(up)) || (st = check_mat(down))) return st;
+        if (I_sh) {
+            if ((st = check_mat(sh_gate)) || (st = check_mat(sh_up)) || (st = check_mat(sh_down)))
+                return st;
+        } else if (sh_gate || sh_up || sh_down) {
+            return MOE_ERR_SHAPE;
+        }
+        if (r && (st = check_routing(r))) return st;
+        if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4)) return MOE_ERR_ALIGN;
+        if ((st = check_ws(ws, ws_bytes, decode_ws_bytes(I, I_sh, k)))) return st;
+        DecodeArgs a{};
+        a.x = x;
+        a.logits = logits;
+        a.H = H;
+        a.I = I;
+        a.I_sh = I_sh;
+        a.E = E;
+        a.k = k;
+        a.gate = to_dev(gate);
+        a.up = to_dev(up);
+        a.down = to_dev(down);
+        a.sh_gate = to_dev(sh_gate);
+        a.sh_up = to_dev(sh_up);
+        a.sh_down = to_dev(sh_down);
+        a.write_routing = r ? 1 : 0;
+        if (r) a.r = to_dev(r);
+        a.max_blocks = max_blocks_of(1, E, k, block_rows);
+        a.h = (uint16_t*)ws;
+        a.y = y;
+        return launch_decode(a, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_decode_q4_sequential(const uint16_t* x, const float* logits, int n_tok, int H, int I,
+                             int I_sh, int E, int k, const moe_q4_mat* gate,
+                             const moe_q4_mat* up, const moe_q4_mat* down,
+                             const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                             const moe_q4_mat* sh_down, uint16_t* y, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    if (n_tok < 1) return MOE_ERR_SHAPE;
+    // validate once through the single-token entry's checks (token 0 pointers)
+    for (int t = 0; t < n_tok; ++t) {
+        const int st = moe_decode_q4(x + (size_t)t * H, logits + (size_t)t * E, H, I, I_sh, E, k,
+                                     32, gate, up, down, sh_gate, sh_up, sh_down, nullptr,
+                                     y + (size_t)t * H, ws, ws_bytes, stream);
+        if (st) return st;
+    }
+    return MOE_OK;
+}
+
 size_t moe_layer_workspace_bytes(int chunk_tokens, int H, int I, int I_sh, int E, int k,
                                  int block_rows) {
     if (check_layer_shape(chunk_tokens, H, I, I_sh, E, k, block_rows)) return 0;

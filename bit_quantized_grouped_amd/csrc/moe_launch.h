@@ -47,6 +47,21 @@ size_t gemm_ws_layout(int T, int I, int I_sh, int k, size_t* off_h, size_t* off_
 hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream);
 
+// decode.hip
+struct DecodeArgs {
+    const uint16_t* x;        // [1, H]
+    const float* logits;      // [1, E]
+    int H, I, I_sh, E, k;
+    QMatDev gate, up, down, sh_gate, sh_up, sh_down;
+    RoutingDev r;
+    int write_routing;
+    int max_blocks;
+    uint16_t* h;              // workspace [k + 1][max(I, I_sh)] bf16
+    uint16_t* y;              // [1, H]
+};
+size_t decode_ws_bytes(int I, int I_sh, int k);
+hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream);
+
 // combine.hip
 hipError_t launch_combine(const uint16_t* expert_out, const uint16_t* shared_out,
                           const int32_t* assign_row, const float* topk_w, int T, int H, int k,

@@ -141,3 +141,24 @@ def test_split_phases_reject_bad_arguments():
     assert dn(eo=MISALIGNED) == bq.MOE_ERR_ALIGN
     assert dn(mats=[_mat(MISALIGNED), m]) == bq.MOE_ERR_ALIGN
     assert dn(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
+
+
+def test_decode_rejects_bad_arguments():
+    L = bq.lib()
+    m = _mat()
+    mats = [ctypes.byref(m)] * 6
+    ws = bq.decode_workspace_bytes(2048, 512, 512, 256, 8)
+    assert ws >= 9 * 512 * 2
+    assert bq.decode_workspace_bytes(2048, 512, 512, 256, 65) == 0     # k > 64
+    call = lambda x=FAKE, k=8, H=2048, y=FAKE, wsb=ws, r=None: L.moe_decode_q4(  # noqa: E731
+        x, FAKE, H, 512, 512, 256, k, 32, *mats, r, y, FAKE, wsb, None)
+    assert call(x=None) == bq.MOE_ERR_NULL
+    assert call(y=None) == bq.MOE_ERR_NULL
+    assert call(k=65) == bq.MOE_ERR_SHAPE
+    assert call(H=2000) == bq.MOE_ERR_SHAPE
+    assert call(y=MISALIGNED) == bq.MOE_ERR_ALIGN
+    assert call(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
+    bad = bq.MoeRouting(*([FAKE.value] * 8 + [None]))
+    assert call(r=ctypes.byref(bad)) == bq.MOE_ERR_NULL
+    assert L.moe_decode_q4_sequential(FAKE, FAKE, 0, 2048, 512, 512, 256, 8, *mats, FAKE, FAKE,
+                                      ws, None) == bq.MOE_ERR_SHAPE

@@ -217,3 +217,67 @@ def test_split_phases_equal_grouped_gemm():
     torch.cuda.synchronize()
     assert np.array_equal(bq.bf16_to_bits(eo), got["expert_out"])
     assert np.array_equal(bq.bf16_to_bits(so), got["shared_out"])
+
+
+# ---------------------------------------------------------------------------
+# Fused single-launch decode (one token per call)
+# ---------------------------------------------------------------------------
+
+def _decode_one(layer, x_bits_row, logits_row, ws=None, with_routing=True):
+    x = bq.bf16_from_bits(x_bits_row, DEV)
+    lg = torch.from_numpy(np.ascontiguousarray(logits_row)).to(DEV)
+    r = bq.DeviceRouting(1, layer.E, layer.k, layer.block_rows, DEV) if with_routing else None
+    y = torch.empty((1, layer.H), dtype=torch.bfloat16, device=DEV)
+    ws = layer.decode(x, lg, y, routing=r, ws=ws)
+    torch.cuda.synchronize()
+    return bq.bf16_to_bits(y), (r.to_host() if r is not None else None), ws
+
+
+def test_fused_decode_workload(big_layer):
+    w, layer = big_layer
+    cfg = CONFIGS["decode"]
+    x_bits, logits = make_activations(cfg)
+    ws = None
+    for t in (0, 1, 2, 125, 500, 999):
+        announce(f"fused decode token {t}")
+        y, r, ws = _decode_one(layer, x_bits[t:t + 1], logits[t:t + 1], ws)
+        ref = oracle_layer(w, cfg, x_bits[t:t + 1], logits[t:t + 1])
+        assert_routing_matches(r, logits[t:t + 1], cfg.k)
+        assert_close_layer(y, ref["y"])
+
+
+def test_fused_decode_sequential_equals_single(big_layer):
+    w, layer = big_layer
+    cfg = CONFIGS["decode"]
+    x_bits, logits = make_activations(cfg)
+    n = 40
+    x = bq.bf16_from_bits(x_bits[:n], DEV)
+    lg = torch.from_numpy(logits[:n]).to(DEV)
+    y = torch.empty((n, cfg.H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(bq.decode_workspace_bytes(cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k),
+                     dtype=torch.uint8, device=DEV)
+    announce("fused decode sequential x40")
+    bq.moe_decode_q4_sequential(x, lg, cfg.I, cfg.I_sh, cfg.k, *layer.weight_mats(), y, ws)
+    torch.cuda.synchronize()
+    ys = bq.bf16_to_bits(y)
+    for t in (0, 17, 39):
+        y1, _, _ = _decode_one(layer, x_bits[t:t + 1], logits[t:t + 1], with_routing=False)
+        assert np.array_equal(ys[t:t + 1], y1)     # same kernel, deterministic
+
+
+@pytest.mark.parametrize("H,I,E,k,I_sh", [
+    (256, 128, 16, 2, 128),      # the tiny layer's shape
+    (512, 256, 100, 7, 0),       # no shared expert, E not a multiple of 64
+    (384, 192, 8, 1, 320),       # I_sh != I, k = 1
+])
+def test_fused_decode_small_shapes(H, I, E, k, I_sh):
+    cfg = small_config(6, H, I, E, k, I_sh, seed=E + k)
+    w = make_weights(cfg, seed=E * 3 + k, cache=False)
+    x_bits, logits = make_activations(cfg)
+    layer = bq.MoeLayer(w, H, I, I_sh, E, k, DEV)
+    for t in range(cfg.T):
+        announce(f"fused decode small H={H} I={I} E={E} k={k} I_sh={I_sh} t={t}")
+        y, r, _ = _decode_one(layer, x_bits[t:t + 1], logits[t:t + 1])
+        ref = oracle_layer(w, cfg, x_bits[t:t + 1], logits[t:t + 1])
+        assert_routing_matches(r, logits[t:t + 1], k)
+        assert_close_layer(y, ref["y"])
