@@ -308,7 +308,7 @@ int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const mo
 
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k) {
     if (check_layer_shape(1, H, I, I_sh, E, k, 32) || k > 64) return 0;
-    return decode_ws_bytes(I, I_sh, k);
+    return decode_ws_layout(I, I_sh, k, nullptr, nullptr);
 }
 
 int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh, int E, int k,
@@ -330,7 +330,9 @@ int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh
         }
         if (r && (st = check_routing(r))) return st;
         if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4)) return MOE_ERR_ALIGN;
-        if ((st = check_ws(ws, ws_bytes, decode_ws_bytes(I, I_sh, k)))) return st;
+        size_t off_idx = 0, off_w = 0;
+        const size_t need = decode_ws_layout(I, I_sh, k, &off_idx, &off_w);
+        if ((st = check_ws(ws, ws_bytes, need))) return st;
         DecodeArgs a{};
         a.x = x;
         a.logits = logits;
@@ -349,6 +351,8 @@ int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh
         if (r) a.r = to_dev(r);
         a.max_blocks = max_blocks_of(1, E, k, block_rows);
         a.h = (uint16_t*)ws;
+        a.sel_idx = (int32_t*)((char*)ws + off_idx);
+        a.sel_w = (float*)((char*)ws + off_w);
         a.y = y;
         return launch_decode(a, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     } catch (...) {

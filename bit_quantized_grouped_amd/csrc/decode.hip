@@ -1,212 +1,321 @@
-// Batch-1 decode of the MoE layer in one launch per token.
+// Batch-1 decode of the MoE layer: two ordinary launches per token, no host
+// synchronisation and no grid-wide barrier.
 //
 // Decode is bound by bytes moved, not by compute ([P3] droneth.or.th,
 // "Decode is limited by bandwidth more than by compute"), and the engine
 // removes per-token host round trips and fuses kernel chains ([P1]
 // dothoosh.com Lily article, "Decode optimizations", kernel-fusion bullet).
-// One cooperative launch covers the whole layer for one token:
-//   0. every workgroup selects the token's top-k from the logits itself
-//      (the same deterministic selection as moe_route), so no barrier is
-//      needed before the expert work; workgroup 0 writes the routing arrays;
-//   1. gate/up rows of the k chosen experts and the shared expert are spread
-//      over all waves: each wave streams whole weight rows (64 lanes x 16 B =
-//      one 1 KB row of codes per load), dequantizes them in registers
-//      (w = bf16_rne(fp32(q*s + b))), dots them with x in fp32 and
-//      writes h = bf16(silu(g) * u);
-//   -- one grid-wide barrier (all workgroups are co-resident) --
-//   2. each wave owns output columns: for every expert it streams that
-//      expert's down-projection row, dots it with h, and accumulates
-//      topk_w * dot (shared expert with weight 1) in fp32; y = bf16(sum).
-#include <hip/hip_cooperative_groups.h>
-
-#include <atomic>
-
+//
+//   decode_gateup_kernel: every workgroup selects the token's top-k from the
+//     logits itself (the same deterministic selection as moe_route; workgroup
+//     0 also publishes it), then its waves stream gate/up weight rows of the
+//     k chosen experts and the shared expert, kGuRows row pairs per wave at a
+//     time, and write h = bf16(silu(g) * u).
+//   decode_down_kernel: each workgroup owns 4 output columns; its 4 waves
+//     split the experts, stream those experts' down-projection rows for the
+//     4 columns, and weight each expert's dot with topk_w (shared expert:
+//     weight 1); the 4 wave partials are summed in a fixed order, y = bf16.
+//
+// The weights are 4-bit groupwise affine, w = q * s + b per 64 weights ([P1]
+// "Prefill optimizations", fused-dequantization bullet; [P3] "A big model
+// that touches only part of its weights per token").  The pages expand them
+// to bf16 because the tensor units take bf16; a batch-1 GEMV does not use the
+// tensor units, and each weight row is read exactly once, so here the
+// per-weight VALU work is what competes with HBM.  Each dot is therefore
+// taken in its exact affine form per group, sum x (q s + b) =
+// s sum q x + b sum x, in fp32: the activations are widened once per pass
+// and shared by every row the wave streams, so a weight costs about two VALU
+// operations (nibble to float, one FMA).  The result differs from a product
+// with bf16-rounded weights only in rounding.
 #include "moe_device.h"
 #include "moe_launch.h"
 #include "moe_topk.h"
 
 namespace moeq4 {
 
-namespace cg = cooperative_groups;
-
-constexpr int kDecThreads = 512;
+constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / WAVE;
 constexpr int kDecMaxK = 64;
+constexpr int kGuRows = 4;    // gate/up row pairs one wave streams together
+constexpr int kDnExp = 3;     // experts whose down rows one wave loads together
+constexpr int kDnCols = 4;    // output columns per down workgroup (16 lanes each)
 
-// Dot of 8 bf16 weights (packed pairs) with 8 bf16 activations (packed pairs):
-// each bf16 is widened to fp32 exactly (its bits are the high half of the
-// fp32) and the products are accumulated with fp32 FMAs.
-__device__ __forceinline__ float dot8(const bf16x8_t& w, const u32x4_t& xv, float acc) {
-    const u32x4_t wv = __builtin_bit_cast(u32x4_t, w);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc = __builtin_fmaf(__builtin_bit_cast(float, wv[i] << 16),
-                             __builtin_bit_cast(float, xv[i] << 16), acc);
-        acc = __builtin_fmaf(__builtin_bit_cast(float, wv[i] & 0xFFFF0000u),
-                             __builtin_bit_cast(float, xv[i] & 0xFFFF0000u), acc);
-    }
-    return acc;
+// q * 2^-9 for the 8 codes of a packed word, in code order (low nibble first).
+__device__ __forceinline__ void codes_unit(uint32_t w, float (&q)[8]) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+    const f32x2_t q02 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const f32x2_t q46 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const f32x2_t q13 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const f32x2_t q57 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    q[0] = q02[0]; q[1] = q13[0]; q[2] = q02[1]; q[3] = q13[1];
+    q[4] = q46[0]; q[5] = q57[0]; q[6] = q46[1]; q[7] = q57[1];
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// 32 bf16 activations (4 x 16 B) widened to fp32 (exact), and their sum.
+__device__ __forceinline__ float widen32(const u32x4_t (&v)[4], float (&f)[32]) {
+    float s = 0.0f;
 #pragma unroll
-    for (int off = WAVE / 2; off >= 1; off >>= 1) v += shfl_xor(v, off);
-    return v;
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t w = v[i / 4][i % 4];
+        f[2 * i] = __builtin_bit_cast(float, w << 16);
+        f[2 * i + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        s += f[2 * i] + f[2 * i + 1];
+    }
+    return s;
+}
+
+// sum_i (q_i * 2^-9) * f_i over the 32 codes of 4 packed words.
+__device__ __forceinline__ float qdot32(const u32x4_t& w, const float (&f)[32]) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float q[8];
+        codes_unit(w[j], q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaf(q[i], f[8 * j + i], a);
+    }
+    return a;
+}
+
+// Butterfly reduction of NV values over the wave.  Afterwards every lane
+// holds the full sum of one value: the top log2(NV) lane bits, read from
+// bit 5 down, are the binary digits of that value's index (most significant
+// first).
+template <int NV>
+__device__ __forceinline__ float wave_reduce_multi(float (&v)[NV], int lane) {
+    int m = WAVE / 2;
+#pragma unroll
+    for (int cnt = NV; cnt > 1; cnt /= 2, m /= 2) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < cnt / 2; ++i) {
+            const float keep = upper ? v[i + cnt / 2] : v[i];
+            const float send = upper ? v[i] : v[i + cnt / 2];
+            v[i] = keep + shfl_xor(send, m);
+        }
+    }
+    float s = v[0];
+    for (; m >= 1; m /= 2) s += shfl_xor(s, m);
+    return s;
+}
+
+// T = 1 routing arrays from the chosen experts (workgroup-uniform call).
+__device__ void write_routing_t1(const DecodeArgs& p, const int* s_idx, const float* s_w,
+                                 int tid) {
+    const int k = p.k;
+    for (int e = tid; e < p.E; e += kDecThreads) p.r.counts[e] = 0;
+    __syncthreads();
+    if (tid < k) {
+        const int e = s_idx[tid];
+        int rank = 0;   // row of assignment tid = number of chosen experts below e
+        for (int j = 0; j < k; ++j) rank += s_idx[j] < e ? 1 : 0;
+        p.r.topk_idx[tid] = e;
+        p.r.topk_w[tid] = s_w[tid];
+        p.r.counts[e] = 1;
+        p.r.sorted_assign[rank] = tid;
+        p.r.assign_row[tid] = rank;
+        p.r.block_expert[rank] = e;
+        p.r.block_row[rank] = rank;
+    }
+    for (int e = tid; e <= p.E; e += kDecThreads) {
+        int off = 0;
+        for (int j = 0; j < k; ++j) off += s_idx[j] < e ? 1 : 0;
+        p.r.offsets[e] = off;
+    }
+    for (int b = k + tid; b < p.max_blocks; b += kDecThreads) {
+        p.r.block_expert[b] = -1;
+        p.r.block_row[b] = -1;
+    }
+    if (tid == 0) p.r.n_blocks[0] = k;
 }
 
 template <int EPL>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p) {
     __shared__ int s_idx[kDecMaxK];
     __shared__ float s_w[kDecMaxK];
     __shared__ uint32_t s_scr[3 * kDecMaxK];
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-    const int k = p.k, H = p.H;
-    const float unit_inv = 1.0f / fp8_unit();
+    const int k = p.k, H = p.H, I = p.I, I_sh = p.I_sh;
 
-    // ---- 0. routing of the token (every workgroup, identical result) ----
     if (wave == 0)
         topk_token<EPL>(p.logits, p.E, k, s_idx, s_w, s_scr, (int*)(s_scr + k),
                         (float*)(s_scr + 2 * k), nullptr);
     __syncthreads();
-    if (blockIdx.x == 0 && p.write_routing) {
-        // T = 1: counts one-hot, rows in ascending expert order, one block per expert
-        for (int e = tid; e < p.E; e += kDecThreads) p.r.counts[e] = 0;
-        __syncthreads();
+    if (blockIdx.x == 0) {
         if (tid < k) {
-            const int e = s_idx[tid];
-            int rank = 0;   // row of assignment tid = number of chosen experts below e
-            for (int j = 0; j < k; ++j) rank += s_idx[j] < e ? 1 : 0;
-            p.r.topk_idx[tid] = e;
-            p.r.topk_w[tid] = s_w[tid];
-            p.r.counts[e] = 1;
-            p.r.sorted_assign[rank] = tid;
-            p.r.assign_row[tid] = rank;
-            p.r.block_expert[rank] = e;
-            p.r.block_row[rank] = rank;
+            p.sel_idx[tid] = s_idx[tid];
+            p.sel_w[tid] = s_w[tid];
         }
-        for (int e = tid; e <= p.E; e += kDecThreads) {
-            int off = 0;
-            for (int j = 0; j < k; ++j) off += s_idx[j] < e ? 1 : 0;
-            p.r.offsets[e] = off;
-        }
-        for (int b = k + tid; b < p.max_blocks; b += kDecThreads) {
-            p.r.block_expert[b] = -1;
-            p.r.block_row[b] = -1;
-        }
-        if (tid == 0) p.r.n_blocks[0] = k;
+        if (p.write_routing) write_routing_t1(p, s_idx, s_w, tid);
     }
 
-    const int gwave = blockIdx.x * kDecWaves + wave;
-    const int nwaves = gridDim.x * kDecWaves;
-    const int ldh = p.I > p.I_sh ? p.I : p.I_sh;
-
-    // ---- 1. gate/up rows -> h ----
-    const int n_routed = k * p.I;
-    const int n_tasks = n_routed + p.I_sh;
-    for (int task = gwave; task < n_tasks; task += nwaves) {
-        const bool sh = task >= n_routed;
-        const int j = sh ? k : task / p.I;
-        const int n = sh ? task - n_routed : task % p.I;
-        const int e = sh ? 0 : s_idx[j];
-        const int N = sh ? p.I_sh : p.I;
-        const QMatDev& g = sh ? p.sh_gate : p.gate;
-        const QMatDev& u = sh ? p.sh_up : p.up;
-        const size_t row = (size_t)e * N + n;
-        float pg = 0.0f, pu = 0.0f;
-        for (int kb = lane * 32; kb < H; kb += WAVE * 32) {
-            const u32x4_t gw = *(const u32x4_t*)(g.codes + row * (H / 8) + kb / 8);
-            const u32x4_t uw = *(const u32x4_t*)(u.codes + row * (H / 8) + kb / 8);
-            const int grp = kb / 64;
-            const float gs = bf16_to_f32(g.scales[row * (H / 64) + grp]) * unit_inv;
-            const float gb = bf16_to_f32(g.biases[row * (H / 64) + grp]);
-            const float us = bf16_to_f32(u.scales[row * (H / 64) + grp]) * unit_inv;
-            const float ub = bf16_to_f32(u.biases[row * (H / 64) + grp]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4_t xv = *(const u32x4_t*)(p.x + kb + 8 * q);
-                pg = dot8(dequant_word(gw[q], gs, gb), xv, pg);
-                pu = dot8(dequant_word(uw[q], us, ub), xv, pu);
-            }
-        }
-        pg = wave_sum(pg);
-        pu = wave_sum(pu);
-        if (lane == 0) p.h[(size_t)j * ldh + n] = __builtin_bit_cast(uint16_t, (__bf16)(silu_f32(pg) * pu));
-    }
-
-    cg::this_grid().sync();
-
-    // ---- 2. down rows of every expert for this wave's columns, weighted sum ----
-    const int half = lane / 32, lq = lane % 32;
-    for (int cp = gwave; cp < H / 2; cp += nwaves) {
-        const int c = 2 * cp + half;
-        float acc = 0.0f;
-        for (int j = 0; j <= k; ++j) {
-            const bool sh = j == k;
-            if (sh && !p.I_sh) break;
-            const int N = sh ? p.I_sh : p.I;   // down K
-            const int e = sh ? 0 : s_idx[j];
-            const float wj = sh ? 1.0f : s_w[j];
-            const QMatDev& d = sh ? p.sh_down : p.down;
-            const size_t row = (size_t)e * H + c;
-            float part = 0.0f;
-            for (int wd = lq; wd < N / 8; wd += 32) {
-                const uint32_t code = d.codes[row * (N / 8) + wd];
-                const int grp = wd / 8;
-                const float s = bf16_to_f32(d.scales[row * (N / 64) + grp]) * unit_inv;
-                const float b = bf16_to_f32(d.biases[row * (N / 64) + grp]);
-                const u32x4_t hv = *(const u32x4_t*)(p.h + (size_t)j * ldh + 8 * wd);
-                part = dot8(dequant_word(code, s, b), hv, part);
-            }
-            acc = __builtin_fmaf(wj, part, acc);
-        }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) acc += shfl_xor(acc, off);
-        if (lq == 0) p.y[c] = __builtin_bit_cast(uint16_t, (__bf16)acc);
-    }
-}
-
-size_t decode_ws_bytes(int I, int I_sh, int k) {
     const int ldh = I > I_sh ? I : I_sh;
-    return align_up((size_t)(k + 1) * ldh * sizeof(uint16_t), 256);
+    const int n_tasks = I_sh + k * I;   // shared-expert rows first, then expert j's rows
+    const float unit_inv = 1.0f / fp8_unit();
+    const int stride = gridDim.x * kDecWaves * kGuRows;
+    for (int t0 = (blockIdx.x * kDecWaves + wave) * kGuRows; t0 < n_tasks; t0 += stride) {
+        const uint32_t* gc[kGuRows];
+        const uint32_t* uc[kGuRows];
+        const uint16_t *gs[kGuRows], *gb[kGuRows], *us[kGuRows], *ub[kGuRows];
+        int hidx[kGuRows];
+#pragma unroll
+        for (int r = 0; r < kGuRows; ++r) {
+            const int t = t0 + r < n_tasks ? t0 + r : n_tasks - 1;   // tail: re-read a valid row
+            const bool sh = t < I_sh;
+            const int j = sh ? k : (t - I_sh) / I;
+            const int n = sh ? t : (t - I_sh) - j * I;
+            const size_t row = sh ? (size_t)n : (size_t)s_idx[j] * I + n;
+            const QMatDev& g = sh ? p.sh_gate : p.gate;
+            const QMatDev& u = sh ? p.sh_up : p.up;
+            gc[r] = g.codes + row * (H / 8);
+            uc[r] = u.codes + row * (H / 8);
+            gs[r] = g.scales + row * (H / 64);
+            gb[r] = g.biases + row * (H / 64);
+            us[r] = u.scales + row * (H / 64);
+            ub[r] = u.biases + row * (H / 64);
+            hidx[r] = t0 + r < n_tasks ? j * ldh + n : -1;
+        }
+        float acc[2 * kGuRows];
+#pragma unroll
+        for (int i = 0; i < 2 * kGuRows; ++i) acc[i] = 0.0f;
+        for (int kb = lane * 32; kb < H; kb += WAVE * 32) {
+            u32x4_t xv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xv[q] = *(const u32x4_t*)(p.x + kb + 8 * q);
+            u32x4_t gw[kGuRows], uw[kGuRows];
+            float sg[kGuRows], bg[kGuRows], su[kGuRows], bu[kGuRows];
+            const int grp = kb / 64;
+#pragma unroll
+            for (int r = 0; r < kGuRows; ++r) {
+                gw[r] = *(const u32x4_t*)(gc[r] + kb / 8);
+                uw[r] = *(const u32x4_t*)(uc[r] + kb / 8);
+                sg[r] = bf16_to_f32(gs[r][grp]);
+                bg[r] = bf16_to_f32(gb[r][grp]);
+                su[r] = bf16_to_f32(us[r][grp]);
+                bu[r] = bf16_to_f32(ub[r][grp]);
+            }
+            float xf[32];
+            const float sx = widen32(xv, xf);
+#pragma unroll
+            for (int r = 0; r < kGuRows; ++r) {
+                acc[r] = __builtin_fmaf(sg[r] * unit_inv, qdot32(gw[r], xf),
+                                        __builtin_fmaf(bg[r], sx, acc[r]));
+                acc[kGuRows + r] = __builtin_fmaf(su[r] * unit_inv, qdot32(uw[r], xf),
+                                                  __builtin_fmaf(bu[r], sx, acc[kGuRows + r]));
+            }
+        }
+        // lane l < 32 now holds g of row (l >> 3) & 3 and lane l + 32 holds u of that row
+        const float gsum = wave_reduce_multi<2 * kGuRows>(acc, lane);
+        const float usum = shfl_xor(gsum, WAVE / 2);
+        const int r = (lane >> 3) & (kGuRows - 1);
+        if (lane < WAVE / 2 && (lane & 7) == 0) {
+            int hi = hidx[0];
+#pragma unroll
+            for (int q = 1; q < kGuRows; ++q) hi = r == q ? hidx[q] : hi;
+            if (hi >= 0) p.h[hi] = __builtin_bit_cast(uint16_t, (__bf16)(silu_f32(gsum) * usum));
+        }
+    }
 }
 
-// Co-resident workgroups per CU for decode_kernel<EPL>, queried once per device.
-template <int EPL>
-static int decode_grid(int device) {
-    // value depends only on the device and the kernel; benign if two threads compute it
-    static std::atomic<int> cache[64];
-    if (device < 0 || device >= 64) return 0;
-    if (!cache[device].load(std::memory_order_relaxed)) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<EPL>, kDecThreads, 0) !=
-                hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-            return 0;
-        const int use = per_cu < 2 ? per_cu : 2;
-        cache[device].store(use * cus, std::memory_order_relaxed);
+__global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) {
+    __shared__ float s_part[kDecWaves][kDnCols];
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int k = p.k, H = p.H, I = p.I, I_sh = p.I_sh;
+    const int ldh = I > I_sh ? I : I_sh;
+    const int nexp = k + (I_sh ? 1 : 0);    // slot k is the shared expert
+    const int c = blockIdx.x * kDnCols + lane / 16;
+    const int kl = (lane % 16) * 32;
+    const float unit_inv = 1.0f / fp8_unit();
+    float acc = 0.0f;
+    for (int j0 = wave; j0 < nexp; j0 += kDecWaves * kDnExp) {
+        const uint32_t* dc[kDnExp];
+        const uint16_t *ds[kDnExp], *db[kDnExp];
+        const uint16_t* hp[kDnExp];
+        float wj[kDnExp];
+        int N[kDnExp];
+#pragma unroll
+        for (int i = 0; i < kDnExp; ++i) {
+            const int j = j0 + i * kDecWaves;
+            const bool on = j < nexp;
+            const bool sh = j == k;
+            const int e = on && !sh ? p.sel_idx[j] : 0;
+            const QMatDev& d = sh ? p.sh_down : p.down;
+            N[i] = !on ? 0 : sh ? I_sh : I;
+            const int Nr = N[i] ? N[i] : 64;
+            const size_t row = (size_t)e * H + c;
+            dc[i] = d.codes + row * (Nr / 8);
+            ds[i] = d.scales + row * (Nr / 64);
+            db[i] = d.biases + row * (Nr / 64);
+            hp[i] = p.h + (size_t)(on ? j : 0) * ldh;
+            wj[i] = on ? (sh ? 1.0f : p.sel_w[j]) : 0.0f;
+        }
+        for (int kb = kl; kb < ldh; kb += 16 * 32) {
+            u32x4_t cw[kDnExp], hv[kDnExp][4];
+            float s[kDnExp], b[kDnExp];
+#pragma unroll
+            for (int i = 0; i < kDnExp; ++i) {
+                if (kb < N[i]) {
+                    cw[i] = *(const u32x4_t*)(dc[i] + kb / 8);
+                    s[i] = bf16_to_f32(ds[i][kb / 64]);
+                    b[i] = bf16_to_f32(db[i][kb / 64]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[i][q] = *(const u32x4_t*)(hp[i] + kb + 8 * q);
+                } else {
+                    cw[i] = u32x4_t{0, 0, 0, 0};
+                    s[i] = 0.0f;
+                    b[i] = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[i][q] = u32x4_t{0, 0, 0, 0};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kDnExp; ++i) {
+                float hf[32];
+                const float hs = widen32(hv[i], hf);
+                const float part = __builtin_fmaf(s[i] * unit_inv, qdot32(cw[i], hf), b[i] * hs);
+                acc = __builtin_fmaf(wj[i], part, acc);
+            }
+        }
     }
-    return cache[device].load(std::memory_order_relaxed);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) acc += shfl_xor(acc, off);
+    if ((lane & 15) == 0) s_part[wave][lane / 16] = acc;
+    __syncthreads();
+    if (tid < kDnCols) {
+        float y = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) y += s_part[w][tid];
+        p.y[blockIdx.x * kDnCols + tid] = __builtin_bit_cast(uint16_t, (__bf16)y);
+    }
+}
+
+size_t decode_ws_layout(int I, int I_sh, int k, size_t* off_sel_idx, size_t* off_sel_w) {
+    const int ldh = I > I_sh ? I : I_sh;
+    const size_t h = align_up((size_t)(k + 1) * ldh * sizeof(uint16_t), 256);
+    if (off_sel_idx) *off_sel_idx = h;
+    if (off_sel_w) *off_sel_w = h + kDecMaxK * sizeof(int32_t);
+    return h + align_up(kDecMaxK * (sizeof(int32_t) + sizeof(float)), 256);
 }
 
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    if (e != hipSuccess) return e;
     const int epl = (args.E + WAVE - 1) / WAVE;
-    void* kargs[1] = {(void*)&args};
-#define MOE_DECODE(N)                                                                         \
-    do {                                                                                      \
-        const int grid = decode_grid<N>(device);                                              \
-        if (grid <= 0) return hipErrorInvalidConfiguration;                                   \
-        return hipLaunchCooperativeKernel((const void*)decode_kernel<N>, dim3(grid),          \
-                                          dim3(kDecThreads), kargs, 0, stream);               \
-    } while (0)
-    if (epl <= 1) MOE_DECODE(1);
-    else if (epl <= 2) MOE_DECODE(2);
-    else if (epl <= 4) MOE_DECODE(4);
-    else if (epl <= 8) MOE_DECODE(8);
-    else MOE_DECODE(16);
-#undef MOE_DECODE
+    const int n_tasks = args.I_sh + args.k * args.I;
+    const int chunks = (n_tasks + kGuRows - 1) / kGuRows;
+    const dim3 gu_grid((chunks + kDecWaves - 1) / kDecWaves);
+#define MOE_DECODE_GU(N) \
+    hipLaunchKernelGGL(decode_gateup_kernel<N>, gu_grid, dim3(kDecThreads), 0, stream, args)
+    if (epl <= 1) MOE_DECODE_GU(1);
+    else if (epl <= 2) MOE_DECODE_GU(2);
+    else if (epl <= 4) MOE_DECODE_GU(4);
+    else if (epl <= 8) MOE_DECODE_GU(8);
+    else MOE_DECODE_GU(16);
+#undef MOE_DECODE_GU
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_down_kernel, dim3(args.H / kDnCols), dim3(kDecThreads), 0, stream,
+                       args);
+    return hipGetLastError();
 }
 
 }  // namespace moeq4

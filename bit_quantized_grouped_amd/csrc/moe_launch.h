@@ -57,9 +57,12 @@ struct DecodeArgs {
     int write_routing;
     int max_blocks;
     uint16_t* h;              // workspace [k + 1][max(I, I_sh)] bf16
+    int32_t* sel_idx;         // workspace [k]: chosen experts, slot order
+    float* sel_w;             // workspace [k]: their weights
     uint16_t* y;              // [1, H]
 };
-size_t decode_ws_bytes(int I, int I_sh, int k);
+// Workspace bytes; offsets of sel_idx and sel_w (h is at offset 0).
+size_t decode_ws_layout(int I, int I_sh, int k, size_t* off_sel_idx, size_t* off_sel_w);
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream);
 
 // combine.hip

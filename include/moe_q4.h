@@ -177,28 +177,31 @@ int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const mo
 /* Device workspace bytes moe_decode_q4 needs (0 on bad shapes). */
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k);
 
-/* Batch-1 decode of the whole layer for ONE token in one launch ([P3]
- * droneth.or.th, "Decode is limited by bandwidth more than by compute";
- * [P1] dothoosh.com "Decode optimizations", kernel-fusion bullet).
+/* Batch-1 decode of the whole layer for ONE token: two kernel launches on
+ * `stream`, no host synchronisation ([P3] droneth.or.th, "Decode is limited
+ * by bandwidth more than by compute"; [P1] dothoosh.com "Decode
+ * optimizations", kernel-fusion bullet).
  * Computes the same function as moe_route + moe_grouped_gemm_q4 +
  * moe_combine at T = 1: top-k of the logits (identical selection and
- * weights), the k routed experts' and the shared expert's SwiGLU FFNs with
- * the 4-bit weights dequantized in registers, and the weighted sum, written
- * to y.  The per-expert outputs are summed in fp32 without the intermediate
- * bf16 rounding of expert_out (y is rounded to bf16 once).
+ * weights), the k routed experts' and the shared expert's SwiGLU FFNs, and
+ * the weighted sum, written to y.  Each weight-row dot is taken in the exact
+ * affine form s * sum(q x) + b * sum(x) per 64-weight group in fp32, and the
+ * per-expert outputs are summed in fp32 without the bf16 rounding of
+ * expert_out, so y matches the three-call path up to rounding (h and y are
+ * bf16, as there).  Deterministic: the same inputs give the same bits.
  *   x bf16 [1, H] (16-byte aligned), logits fp32 [1, E], y bf16 [1, H]
  *   r: routing arrays of this token (T = 1, block_rows as given), written
  *      exactly as moe_route would; may be NULL to skip them
- *   ws: at least moe_decode_workspace_bytes() bytes, 256-byte aligned
- * Limits: k <= 64.  Launched cooperatively (all workgroups co-resident; one
- * grid-wide barrier between the gate/up and down phases). */
+ *   ws: at least moe_decode_workspace_bytes() bytes, 256-byte aligned;
+ *      holds h and the chosen experts between the two launches
+ * Limits: k <= 64. */
 int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh, int E, int k,
                   int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
                   const moe_q4_mat* down, const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
                   const moe_q4_mat* sh_down, const moe_routing* r, uint16_t* y, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 
-/* n_tok independent batch-1 decode calls, one launch each, enqueued back to
+/* n_tok independent batch-1 decode calls, enqueued back to
  * back on `stream` (token t uses row t of x, logits and y; no batching across
  * tokens, no host synchronisation).  Same per-token result as moe_decode_q4
  * with r = NULL; the workspace is reused by each token in stream order. */
