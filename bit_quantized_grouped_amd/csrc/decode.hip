@@ -135,7 +135,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
     __shared__ int s_idx[kDecMaxK];
     __shared__ float s_w[kDecMaxK];
     __shared__ uint32_t s_scr[3 * kDecMaxK];
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    // wave-uniform from here on, so row addresses stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int k = p.k, H = p.H, I = p.I, I_sh = p.I_sh;
 
     if (wave == 0)
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
             const bool sh = t < I_sh;
             const int j = sh ? k : (t - I_sh) / I;
             const int n = sh ? t : (t - I_sh) - j * I;
-            const size_t row = sh ? (size_t)n : (size_t)s_idx[j] * I + n;
+            const size_t row = sh ? (size_t)n : (size_t)__builtin_amdgcn_readfirstlane(s_idx[j]) * I + n;
             const QMatDev& g = sh ? p.sh_gate : p.gate;
             const QMatDev& u = sh ? p.sh_up : p.up;
             gc[r] = g.codes + row * (H / 8);
@@ -220,7 +222,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
 
 __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) {
     __shared__ float s_part[kDecWaves][kDnCols];
-    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int k = p.k, H = p.H, I = p.I, I_sh = p.I_sh;
     const int ldh = I > I_sh ? I : I_sh;
     const int nexp = k + (I_sh ? 1 : 0);    // slot k is the shared expert

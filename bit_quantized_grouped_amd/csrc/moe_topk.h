@@ -7,6 +7,10 @@
 
 namespace moeq4 {
 
+// Up to this k the selection runs as k wave-argmax rounds, above it as a
+// 32-step radix select followed by an O(k^2) ranking.
+constexpr int kRoundsMaxK = 16;
+
 // Order-preserving map of a finite float to uint32 (-0.0 folded onto +0.0).
 __device__ __forceinline__ uint32_t float_key(float v) {
     const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
@@ -17,8 +21,74 @@ __device__ __forceinline__ int wave_popc_ge(uint32_t key, uint32_t th, bool vali
     return __popcll(__ballot(valid && key >= th));
 }
 
+// Largest key over the wave, returned uniform.  DPP: row_shr 1, 2, 4, 8 leave
+// each row's maximum in its lane 15; row_bcast 15 and 31 carry those into
+// lane 63.  Lanes a shift does not reach keep their own value (max is
+// idempotent, so overlapping windows are harmless).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define MOE_DPP_MAX(ctrl, rows)                                                           \
+    v = __builtin_elementwise_max(                                                        \
+        v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rows, 0xf, false))
+    MOE_DPP_MAX(0x111, 0xf);   // row_shr:1
+    MOE_DPP_MAX(0x112, 0xf);   // row_shr:2
+    MOE_DPP_MAX(0x114, 0xf);   // row_shr:4
+    MOE_DPP_MAX(0x118, 0xf);   // row_shr:8
+    MOE_DPP_MAX(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    MOE_DPP_MAX(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef MOE_DPP_MAX
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Inverse of float_key.
+__device__ __forceinline__ float key_float(uint32_t key) {
+    return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// k rounds of "largest remaining key, lowest expert index among equals": the
+// rounds produce the slots in order (value descending, index ascending), and
+// the renormalised softmax weights come from the k chosen values.  Lane l
+// holds experts l*EPL .. l*EPL+EPL-1; used or absent experts carry key 0.
+// Costs about k * (3 EPL + 25) VALU operations, so it is used for small k.
+template <int EPL>
+__device__ __forceinline__ void topk_rounds(uint32_t (&key)[EPL], int k, int32_t* out_idx,
+                                            float* out_w, int* lds_idx) {
+    const int lane = __lane_id();
+    int my_e = 0;
+    float my_x = 0.0f, v0 = 0.0f, sum = 0.0f;
+    for (int r = 0; r < k; ++r) {
+        uint32_t bk = key[0];
+        int bj = 0;
+#pragma unroll
+        for (int j = 1; j < EPL; ++j) {
+            const bool gt = key[j] > bk;   // strict: the lower index wins a tie
+            bk = gt ? key[j] : bk;
+            bj = gt ? j : bj;
+        }
+        const uint32_t m = wave_max_u32(bk);
+        const int w = __builtin_ctzll(__ballot(bk == m));          // lowest lane holding m
+        const int jw = __builtin_amdgcn_readlane(bj, w);
+        const float val = key_float(m);
+        if (r == 0) v0 = val;
+        const float x = __expf(val - v0);
+        sum += x;
+        if (lane == r) {
+            my_e = w * EPL + jw;
+            my_x = x;
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) key[j] = (lane == w && j == jw) ? 0u : key[j];
+    }
+    if (lane < k) {
+        out_idx[lane] = my_e;
+        out_w[lane] = my_x * (1.0f / sum);
+        if (lds_idx) lds_idx[lane] = my_e;
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Top-k of one token's E logits by one wave.  Lane l holds experts
-// l*EPL .. l*EPL+EPL-1.  s_key/s_e/s_v: this wave's LDS scratch of k entries.
+// l*EPL .. l*EPL+EPL-1.  s_key/s_e/s_v: this wave's LDS scratch of k entries
+// (used when k > kRoundsMaxK).
 template <int EPL>
 __device__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* out_idx,
                            float* out_w, uint32_t* s_key, int* s_e, float* s_v,
@@ -33,6 +103,10 @@ __device__ void topk_token(const float* __restrict__ row, int E, int k, int32_t*
         ok[j] = e < E;
         v[j] = ok[j] ? row[e] : 0.0f;
         key[j] = ok[j] ? float_key(v[j]) : 0u;
+    }
+    if (k <= kRoundsMaxK) {
+        topk_rounds<EPL>(key, k, out_idx, out_w, lds_idx);
+        return;
     }
     // radix select: largest th with count(key >= th) >= k
     uint32_t th = 0;

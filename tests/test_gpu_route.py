@@ -59,6 +59,9 @@ def _tie_heavy(T, E, levels, seed):
     (129, 100, 7, 3, 5),       # E not a multiple of 64
     (40, 1000, 8, 6, 6),       # E up to 1000 (16 experts per lane)
     (5, 1, 1, 1, 7),           # one expert
+    (20, 256, 24, 4, 8),       # k above the round-based selection's limit (radix path)
+    (10, 128, 64, 3, 9),       # largest k
+    (12, 300, 16, 2, 10),      # k at the round-based limit, EPL = 5
 ])
 def test_route_ties(T, E, k, levels, seed):
     L = _tie_heavy(T, E, levels, seed)
