@@ -49,101 +49,165 @@ __global__ __launch_bounds__(kTopkWaves * WAVE) void route_topk_kernel(
                         topk_w + (size_t)t * k, s_key, s_e, s_v);
 }
 
-// Expert of each assignment inside a 64-lane chunk -> (rank among equal
-// experts in lower lanes, number of equal experts in the chunk).
-__device__ __forceinline__ void match_rank(int e, bool valid, int nbits, int* rank, int* cnt) {
+// Lanes of a 64-lane chunk holding the same expert as this lane (expert ids
+// below 2^kExpertBits; E <= 1000).  Bits at or above nbits are zero in every
+// id, so the loop stops there.
+constexpr int kExpertBits = 10;
+__device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
     uint64_t match = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
+#pragma unroll
+    for (int bit = 0; bit < kExpertBits; ++bit) {
+        if (bit >= nbits) break;   // uniform
         const bool set = (e >> bit) & 1;
         const uint64_t bal = __ballot(valid && set);
         match &= set ? bal : ~bal;
     }
-    *rank = __popcll(match & lanemask_lt());
-    *cnt = __popcll(match);
+    return match;
 }
 
-// Exclusive scan of one value per thread over a kGroupThreads workgroup.
-__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+// Exclusive scan of two values per thread over a kGroupThreads workgroup
+// (s_wave: 2 * (kGroupWaves + 1) ints).  Returns the scans of a and b and
+// both totals.
+__device__ void block_exclusive_scan2(int a, int b, int* s_wave, int* ex_a, int* ex_b,
+                                      int* tot_a, int* tot_b) {
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    int incl = v;
+    int ia = a, ib = b;
 #pragma unroll
     for (int off = 1; off < WAVE; off <<= 1) {
-        const int o = __shfl_up(incl, off, WAVE);
-        if (lane >= off) incl += o;
+        const int oa = __shfl_up(ia, off, WAVE);
+        const int ob = __shfl_up(ib, off, WAVE);
+        if (lane >= off) {
+            ia += oa;
+            ib += ob;
+        }
     }
-    if (lane == WAVE - 1) s_wave[wave] = incl;
+    if (lane == WAVE - 1) {
+        s_wave[wave] = ia;
+        s_wave[kGroupWaves + 1 + wave] = ib;
+    }
     __syncthreads();
     if (wave == 0) {
-        int w = lane < kGroupWaves ? s_wave[lane] : 0;
-        int wi = w;
+        const int wa = lane < kGroupWaves ? s_wave[lane] : 0;
+        const int wb = lane < kGroupWaves ? s_wave[kGroupWaves + 1 + lane] : 0;
+        int xa = wa, xb = wb;
 #pragma unroll
-        for (int off = 1; off < WAVE; off <<= 1) {
-            const int o = __shfl_up(wi, off, WAVE);
-            if (lane >= off) wi += o;
+        for (int off = 1; off < kGroupWaves; off <<= 1) {
+            const int oa = __shfl_up(xa, off, WAVE);
+            const int ob = __shfl_up(xb, off, WAVE);
+            if (lane >= off) {
+                xa += oa;
+                xb += ob;
+            }
         }
-        if (lane < kGroupWaves) s_wave[lane] = wi - w;
-        if (lane == kGroupWaves - 1) s_wave[kGroupWaves] = wi;
+        if (lane < kGroupWaves) {
+            s_wave[lane] = xa - wa;
+            s_wave[kGroupWaves + 1 + lane] = xb - wb;
+        }
+        if (lane == kGroupWaves - 1) {
+            s_wave[kGroupWaves] = xa;
+            s_wave[2 * kGroupWaves + 1] = xb;
+        }
     }
     __syncthreads();
-    const int res = s_wave[wave] + incl - v;
-    *total = s_wave[kGroupWaves];
+    *ex_a = s_wave[wave] + ia - a;
+    *ex_b = s_wave[kGroupWaves + 1 + wave] + ib - b;
+    *tot_a = s_wave[kGroupWaves];
+    *tot_b = s_wave[2 * kGroupWaves + 1];
     __syncthreads();
-    return res;
 }
 
 // Histogram, scan, block map and stable scatter of n = T*k assignments
 // whose experts are eids[0..n).  Needs kGroupThreads threads and
-// kGroupWaves*E + kGroupWaves + 1 ints of LDS at s_hist.
+// kGroupWaves*E + 2*(kGroupWaves+1) ints of LDS at s_hist.
+//
+// Wave w owns the contiguous segment w of the assignments and walks it 64 at
+// a time.  Inside a chunk, lanes with equal experts are found by ballots over
+// the expert-id bits; the lowest such lane (the leader) speaks for them.
+// Pass 1: leaders add their group's size to the wave's LDS histogram.  Pass 2:
+// leaders take their group's first row with a returning LDS add on the
+// running per-expert row (seeded with offset + the rows of lower segments)
+// and hand it to their group; a lane's row is that plus its rank among equal
+// experts in lower lanes.  A wave's LDS operations execute in program order,
+// so rows follow assignment order within each expert: a stable counting
+// sort.  When a segment fits in one batch of kPre chunks, its expert ids and
+// match masks stay in registers between the two passes.
 __device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int max_blocks,
                           const RoutingDev& r, int* s_hist) {
+    constexpr int kPre = 16;
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     int* s_wave = s_hist + kGroupWaves * E;
     const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
     const int seg = (n + kGroupWaves - 1) / kGroupWaves;
     const int a_begin = min(n, wave * seg), a_end = min(n, a_begin + seg);
     int* my_hist = s_hist + wave * E;
+    const uint64_t lt = lanemask_lt();
 
     for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) s_hist[i] = 0;
     __syncthreads();
 
-    // pass 1: per-segment histograms.  The segment is walked 64 assignments
-    // at a time; up to kPre chunks of expert ids are fetched ahead into
-    // registers so one memory latency covers kPre chunks.
-    constexpr int kPre = 16;
-    for (int sb = a_begin; sb < a_end; sb += kPre * WAVE) {
-        int ids[kPre];
+    auto load_ids = [&](int sb, int (&ids)[kPre]) {
 #pragma unroll
         for (int q = 0; q < kPre; ++q) {
             const int a = sb + q * WAVE + lane;
             ids[q] = a < a_end ? eids[a] : 0;
         }
+    };
+    auto count = [&](int sb, const int (&ids)[kPre], uint64_t (&mm)[kPre]) {
 #pragma unroll
         for (int q = 0; q < kPre; ++q) {
             const int base = sb + q * WAVE;
             if (base >= a_end) break;
             const bool valid = base + lane < a_end;
-            int rank, cnt;
-            match_rank(ids[q], valid, nbits, &rank, &cnt);
-            if (valid && rank == 0) my_hist[ids[q]] += cnt;
-            __builtin_amdgcn_wave_barrier();
+            mm[q] = match_mask(ids[q], valid, nbits);
+            if (valid && (mm[q] & lt) == 0) atomicAdd(&my_hist[ids[q]], __popcll(mm[q]));
+        }
+    };
+    auto scatter = [&](int sb, const int (&ids)[kPre], const uint64_t (&mm)[kPre]) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int base = sb + q * WAVE;
+            if (base >= a_end) break;
+            const int a = base + lane;
+            const bool valid = a < a_end;
+            const uint64_t m = mm[q];
+            int first = 0;
+            if (valid && (m & lt) == 0) first = atomicAdd(&my_hist[ids[q]], __popcll(m));
+            const int leader = valid ? __builtin_ctzll(m) : lane;
+            first = __shfl(first, leader, WAVE);
+            if (valid) {
+                const int row = first + __popcll(m & lt);
+                r.sorted_assign[row] = a;
+                r.assign_row[a] = row;
+            }
+        }
+    };
+
+    // pass 1: per-segment histograms
+    const bool one_batch = a_end - a_begin <= kPre * WAVE;   // uniform per wave
+    int ids[kPre];
+    uint64_t mm[kPre];
+    if (one_batch) {
+        load_ids(a_begin, ids);
+        count(a_begin, ids, mm);
+    } else {
+        for (int sb = a_begin; sb < a_end; sb += kPre * WAVE) {
+            load_ids(sb, ids);
+            count(sb, ids, mm);
         }
     }
     __syncthreads();
 
     // per expert: prefix over segments, totals, scans, block map
     const int e = tid;
+    int h[kGroupWaves];
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) h[w] = e < E ? s_hist[w * E + e] : 0;
     int cnt = 0;
-    if (e < E) {
-        for (int w = 0; w < kGroupWaves; ++w) {
-            const int h = s_hist[w * E + e];
-            s_hist[w * E + e] = cnt;
-            cnt += h;
-        }
-    }
-    int total_rows, total_blocks;
-    const int off = block_exclusive_scan(e < E ? cnt : 0, s_wave, &total_rows);
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) cnt += h[w];
     const int nb = e < E ? (cnt + block_rows - 1) / block_rows : 0;
-    const int bstart = block_exclusive_scan(nb, s_wave, &total_blocks);
+    int off, bstart, total_rows, total_blocks;
+    block_exclusive_scan2(cnt, nb, s_wave, &off, &bstart, &total_rows, &total_blocks);
     if (e < E) {
         r.counts[e] = cnt;
         r.offsets[e] = off;
@@ -151,7 +215,12 @@ __device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int
             r.block_expert[bstart + i] = e;
             r.block_row[bstart + i] = off + block_rows * i;
         }
-        for (int w = 0; w < kGroupWaves; ++w) s_hist[w * E + e] += off;
+        int run = off;
+#pragma unroll
+        for (int w = 0; w < kGroupWaves; ++w) {
+            s_hist[w * E + e] = run;
+            run += h[w];
+        }
     }
     if (e == 0) {
         r.offsets[E] = total_rows;
@@ -163,32 +232,18 @@ __device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int
     }
     __syncthreads();
 
-    // pass 2: stable scatter (same walk; ranks continue from the segment bases)
-    for (int sb = a_begin; sb < a_end; sb += kPre * WAVE) {
-        int ids[kPre];
-#pragma unroll
-        for (int q = 0; q < kPre; ++q) {
-            const int a = sb + q * WAVE + lane;
-            ids[q] = a < a_end ? eids[a] : 0;
-        }
-#pragma unroll
-        for (int q = 0; q < kPre; ++q) {
-            const int base = sb + q * WAVE;
-            if (base >= a_end) break;
-            const int a = base + lane;
-            const bool valid = a < a_end;
-            const int ea = ids[q];
-            int rank, c;
-            match_rank(ea, valid, nbits, &rank, &c);
-            int row = 0;
-            if (valid) row = my_hist[ea] + rank;
-            __builtin_amdgcn_wave_barrier();
-            if (valid) {
-                if (rank == 0) my_hist[ea] = row + c;
-                r.sorted_assign[row] = a;
-                r.assign_row[a] = row;
+    // pass 2: stable scatter
+    if (one_batch) {
+        scatter(a_begin, ids, mm);
+    } else {
+        for (int sb = a_begin; sb < a_end; sb += kPre * WAVE) {
+            load_ids(sb, ids);
+            #pragma unroll
+            for (int q = 0; q < kPre; ++q) {
+                const int base = sb + q * WAVE;
+                mm[q] = base < a_end ? match_mask(ids[q], base + lane < a_end, nbits) : 0;
             }
-            __builtin_amdgcn_wave_barrier();
+            scatter(sb, ids, mm);
         }
     }
 }
@@ -208,8 +263,8 @@ __global__ __launch_bounds__(kGroupThreads) void route_fused_kernel(
     RoutingDev r) {
     extern __shared__ int smem_i[];
     const int wave = threadIdx.x / WAVE;
-    int* s_hist = smem_i;                                  // kGroupWaves*E + kGroupWaves + 1
-    int* s_eids = s_hist + kGroupWaves * E + kGroupWaves + 1;   // T*k
+    int* s_hist = smem_i;                                  // kGroupWaves*E + 2*(kGroupWaves+1)
+    int* s_eids = s_hist + kGroupWaves * E + 2 * (kGroupWaves + 1);   // T*k
     uint32_t* s_scr = (uint32_t*)(s_eids + T * k) + wave * 3 * k;
     for (int t = wave; t < T; t += kGroupWaves) {
         topk_token<EPL>(logits + (size_t)t * E, E, k, r.topk_idx + (size_t)t * k,
@@ -230,7 +285,7 @@ size_t route_ws_layout(int T, int E, int k, size_t* off_hist, size_t* off_rank) 
 }
 
 static size_t group_lds_bytes(int E) {
-    return (size_t)(kGroupWaves * E + kGroupWaves + 1) * sizeof(int);
+    return (size_t)(kGroupWaves * E + 2 * (kGroupWaves + 1)) * sizeof(int);
 }
 
 static size_t fused_lds_bytes(int T, int E, int k) {
