@@ -118,9 +118,17 @@ struct Streams {
     int sub_c;                        // byte stride of 16 rows in codes
 };
 
+// Chunks past the last one (pipeline run-out) are requested with kVoffOob
+// added to the lane offset: such a load lies outside the buffer resource and
+// returns zeros without touching memory.  Every pipeline step thus issues the
+// same loads, which lets the compiler count the loads in flight across the
+// loop and wait only for the chunk it is about to use (with conditional
+// loads it waits for all of them once per pass over the register ring).
+constexpr int kVoffOob = 0x40000000;
+
 template <int NMAT, int NSUB, int KC>
 __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32>& B,
-                                       const Streams<NMAT, NSUB, KC>& S, int c) {
+                                       const Streams<NMAT, NSUB, KC>& S, int c, int voff_oob) {
     constexpr int W = KC / 32;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -131,11 +139,12 @@ __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32>& B,
 #pragma unroll
                 for (int j = 0; j < W / 4; ++j)
                     B.w[m][s][j] = __builtin_bit_cast(
-                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(S.codes[m], S.voff_c + 16 * j,
-                                                                        so_c, 0));
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                     S.codes[m], S.voff_c + voff_oob + 16 * j, so_c, 0));
             } else {
                 B.w2[m][s] = __builtin_bit_cast(
-                    u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(S.codes[m], S.voff_c, so_c, 0));
+                    u32x2_t,
+                    __builtin_amdgcn_raw_buffer_load_b64(S.codes[m], S.voff_c + voff_oob, so_c, 0));
             }
         }
 }
@@ -315,46 +324,52 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         a_voff[i] = s_row[row] * lda * 2 + c8 * 16;
         a_lds[i] = row * LDA + c8 * 8;
     }
-    auto load_a = [&](u32x4_t (&dst)[APT], int c) {
+    constexpr bool kAllA = A_PIECES % NT == 0;   // every thread holds APT pieces
+    auto load_a = [&](u32x4_t (&dst)[APT], int c, int voff_oob) {
 #pragma unroll
         for (int i = 0; i < APT; ++i)
-            if (a_ok[i])
+            if (kAllA || a_ok[i])
                 dst[i] = __builtin_bit_cast(
-                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff[i], c * KC * 2, 0));
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff[i] + voff_oob,
+                                                                    c * KC * 2, 0));
     };
     auto store_a = [&](const u32x4_t (&src)[APT], uint16_t* dst) {
 #pragma unroll
         for (int i = 0; i < APT; ++i)
-            if (a_ok[i]) *(u32x4_t*)(dst + a_lds[i]) = src[i];
+            if (kAllA || a_ok[i]) *(u32x4_t*)(dst + a_lds[i]) = src[i];
     };
 
     const int nchunks = K / KC;
     // Register pipeline over K-chunks: the A rows and code words of chunk c
     // live in Aq/Bq[c % DEPTH] and are requested DEPTH-1 chunks before the
     // chunk's math, so no load latency sits between two barriers.  A chunk c
-    // is staged into LDS buffer c % 2 one chunk ahead of its math.
+    // is staged into LDS buffer c % 2 one chunk ahead of its math.  Requests
+    // past the last chunk go out of bounds (kVoffOob) and are never used.
     BChunk<NMAT, NSUB, W> Bq[DEPTH];
     u32x4_t Aq[DEPTH][APT];
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d)
-        if (d < nchunks) {
-            load_a(Aq[d], d);
-            load_b<NMAT, NSUB, KC>(Bq[d], S, d);
-        }
+    for (int d = 0; d < DEPTH - 1; ++d) {
+        const int oob = d < nchunks ? 0 : kVoffOob;
+        load_a(Aq[d], d, oob);
+        load_b<NMAT, NSUB, KC>(Bq[d], S, d, oob);
+    }
     store_a(Aq[0], sA);
     __syncthreads();
     for (int c0 = 0; c0 < nchunks; c0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int c = c0 + d;
-            if (c >= nchunks) break;
-            if (c + DEPTH - 1 < nchunks) {
-                load_a(Aq[(d + DEPTH - 1) % DEPTH], c + DEPTH - 1);
-                load_b<NMAT, NSUB, KC>(Bq[(d + DEPTH - 1) % DEPTH], S, c + DEPTH - 1);
+            const int cp = c + DEPTH - 1;
+            const int oob = cp < nchunks ? 0 : kVoffOob;
+            load_a(Aq[(d + DEPTH - 1) % DEPTH], cp, oob);
+            load_b<NMAT, NSUB, KC>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
+            if (c < nchunks) {
+                compute_chunk<NMAT, MT, KC, NSUB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane,
+                                                  sBi_lane, GS, mstride, c * KC / 64, unit_inv, nl,
+                                                  g, msub_act, acc);
+                // after the last chunk this stages unused data into the idle buffer
+                store_a(Aq[(d + 1) % DEPTH], sA + ((c + 1) & 1) * MT * LDA);
             }
-            compute_chunk<NMAT, MT, KC, NSUB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane, sBi_lane, GS,
-                                              mstride, c * KC / 64, unit_inv, nl, g, msub_act, acc);
-            if (c + 1 < nchunks) store_a(Aq[(d + 1) % DEPTH], sA + ((c + 1) & 1) * MT * LDA);
             __syncthreads();
         }
     }
