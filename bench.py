@@ -7,6 +7,13 @@ Prints ONE JSON line.  The 2048-token prefill, batch-1 decode over 1000
 tokens and the skewed 8192-token prefill in chunks of 2048 are timed too and
 reported under "extra".
 
+Warm and cold: repeating one layer lets part of its 455 MB of packed weights
+stay in the 256 MB Infinity Cache between calls.  The cold figures cycle
+through 4 layer copies with distinct weight bytes (1.8 GB), call i on copy
+i mod 4, as consecutive layers of a model would.  Copies 1-3 are made on the
+device from copy 0 by XOR-ing every code word with a per-copy constant and
+copying the scales and biases: same shapes and routing, different bytes.
+
 --calibrate-copy MB runs only a plain device-to-device copy of MB megabytes
 (five times); rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE over it gives the
 scale between those counters and true bytes.
@@ -119,6 +126,22 @@ def main():
     layer = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
     log("weights resident")
     br = layer.block_rows
+    mats0 = layer.weight_mats()
+    layers = [layer] + [
+        bq.MoeLayer.from_device(
+            [None if m is None else bq.DeviceQMat(m.codes ^ (0x01010101 * i), m.scales.clone(),
+                                                  m.biases.clone()) for m in mats0],
+            cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
+        for i in range(1, 4)]
+    log("4 layer copies resident (cold runs)")
+
+    def cold(fn_of_layer):
+        state = [0]
+
+        def step():
+            fn_of_layer(layers[state[0] % len(layers)])
+            state[0] += 1
+        return step
 
     def prep(c):
         xb, lg = make_activations(c)
@@ -128,6 +151,7 @@ def main():
     x, lg = prep(cfg)
     T = cfg.T
     ms = timed(lambda: layer.forward(x, lg), args.steps, args.warmup, torch)
+    ms_cold = timed(cold(lambda L: L.forward(x, lg)), args.steps, args.warmup, torch)
     bufs = layer.buffers(T)
     counts = bufs["routing"].counts.cpu().numpy()
     touched = int(np.count_nonzero(counts))
@@ -187,11 +211,13 @@ def main():
                   "algorithmic_bytes": layer_bytes, "algorithmic_flops": flops,
                   "roofline_frac": t_roof / t_layer,
                   "mfma_frac": flops / t_layer / MFMA_BF16_PEAK,
-                  "hbm_frac": layer_bytes / t_layer / HBM_PEAK},
+                  "hbm_frac": layer_bytes / t_layer / HBM_PEAK,
+                  "cold_tokens_per_s": T / (ms_cold * 1e-3), "cold_us_per_call": ms_cold * 1e3,
+                  "cold_hbm_frac": layer_bytes / (ms_cold * 1e-3) / HBM_PEAK},
     }
     log(f"prefill512: {ms*1e3:.1f} us/call, {T/t_layer:,.0f} tok/s | route {t_route*1e6:.1f} "
         f"gateup {t_gu*1e6:.1f} ({achieved/1e9:.0f} GB/s) down {t_dn*1e6:.1f} "
-        f"combine {t_comb*1e6:.1f} us")
+        f"combine {t_comb*1e6:.1f} us; cold {ms_cold*1e3:.1f} us/call")
 
     # ---------------- secondary workloads ----------------
     extra = {}
@@ -201,6 +227,7 @@ def main():
             c = CONFIGS["prefill2048"]
             x2, lg2 = prep(c)
             ms2 = timed(lambda: layer.forward(x2, lg2), max(10, args.steps // 4), 5, torch)
+            ms2c = timed(cold(lambda L: L.forward(x2, lg2)), max(10, args.steps // 4), 5, torch)
             cnt = layer.buffers(c.T)["routing"].counts.cpu().numpy()
             tch = int(np.count_nonzero(cnt))
             fl = layer_flops(c.T, c.H, c.I, c.k, c.I_sh)
@@ -209,9 +236,11 @@ def main():
             extra["prefill2048"] = {"tokens_per_s": c.T / t, "us_per_call": ms2 * 1e3,
                                     "mfma_frac": fl / t / MFMA_BF16_PEAK,
                                     "hbm_frac": by / t / HBM_PEAK,
-                                    "roofline_frac": max(fl / MFMA_BF16_PEAK, by / HBM_PEAK) / t}
+                                    "roofline_frac": max(fl / MFMA_BF16_PEAK, by / HBM_PEAK) / t,
+                                    "cold_tokens_per_s": c.T / (ms2c * 1e-3),
+                                    "cold_us_per_call": ms2c * 1e3}
             log(f"prefill2048: {ms2*1e3:.1f} us/call, {c.T/t:,.0f} tok/s, "
-                f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%")
+                f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%; cold {ms2c*1e3:.1f} us/call")
             del x2, lg2
         if not only or "decode" in only:
             c = CONFIGS["decode"]
@@ -234,13 +263,44 @@ def main():
                     layer.forward(xs[i], ls[i])
 
             t_three = timed(run_tokens, 2, 1, torch) * 1e-3 / 100
+
+            # cold: token t on layer copy t mod 4.  The 1000 single-token calls are
+            # captured once into a graph (no memset nodes) so the host does not pace
+            # them; each replay is checked bit for bit against the same calls run eagerly.
+            def decode_calls(y_out):
+                for t in range(c.T):
+                    L = layers[t % len(layers)]
+                    bq.moe_decode_q4(xd[t:t + 1], lgd[t:t + 1], c.I, c.I_sh, c.k, L.block_rows,
+                                     *L.weight_mats(), None, y_out[t:t + 1], wsd)
+            y_eager = torch.empty_like(yd)
+            decode_calls(y_eager)
+            y_graph = torch.zeros_like(yd)
+            graph = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph):
+                decode_calls(y_graph)
+            torch.cuda.synchronize()
+            graph_ok = True
+            for _ in range(2):
+                y_graph.zero_()
+                graph.replay()
+                torch.cuda.synchronize()
+                graph_ok &= bool(torch.equal(y_graph.view(torch.int16), y_eager.view(torch.int16)))
+            t_cold = timed(graph.replay, 3, 1, torch) * 1e-3 / c.T
+            del graph
             extra["decode"] = {"tokens_per_s": 1.0 / t_tok, "us_per_token": t_tok * 1e6,
                                "hbm_frac": by_tok / t_tok / HBM_PEAK,
                                "algorithmic_bytes_per_token": by_tok,
-                               "path": "moe_decode_q4: one cooperative launch per token",
+                               "path": "moe_decode_q4: two launches per token "
+                                       "(top-k + gate/up + SwiGLU, then down + weighted sum)",
                                "three_call_us_per_token": t_three * 1e6,
-                               "note": "1000 single-token calls back to back, same layer (warm caches)"}
-            log(f"decode: {t_tok*1e6:.2f} us/token (fused), HBM {100*by_tok/t_tok/HBM_PEAK:.1f}%; "
+                               "cold_us_per_token": t_cold * 1e6,
+                               "cold_hbm_frac": by_tok / t_cold / HBM_PEAK,
+                               "cold_graph_matches_eager": graph_ok,
+                               "note": "warm: 1000 single-token calls back to back on one layer; "
+                                       "cold: token t on layer copy t mod 4, replayed from a graph"}
+            log(f"decode: {t_tok*1e6:.2f} us/token, HBM {100*by_tok/t_tok/HBM_PEAK:.1f}%; "
+                f"cold {t_cold*1e6:.2f} us/token (graph == eager: {graph_ok}); "
                 f"three-call path {t_three*1e6:.1f} us/token")
         if not only or "skew8192" in only:
             c = CONFIGS["skew8192"]

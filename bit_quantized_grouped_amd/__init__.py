@@ -292,6 +292,19 @@ class MoeLayer:
                                                   up(weights.sh_down))
         self._bufs = {}
 
+    @classmethod
+    def from_device(cls, mats, H: int, I: int, I_sh: int, E: int, k: int, device,
+                    block_rows: int = 32) -> "MoeLayer":
+        """A layer over device-resident DeviceQMat objects (gate, up, down, sh_gate, sh_up,
+        sh_down; the shared three may be None)."""
+        layer = cls.__new__(cls)
+        layer.H, layer.I, layer.I_sh, layer.E, layer.k = H, I, I_sh, E, k
+        layer.block_rows = block_rows
+        layer.device = torch.device(device)
+        (layer.gate, layer.up, layer.down, layer.sh_gate, layer.sh_up, layer.sh_down) = mats
+        layer._bufs = {}
+        return layer
+
     def weight_mats(self):
         return (self.gate, self.up, self.down, self.sh_gate, self.sh_up, self.sh_down)
 
