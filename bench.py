@@ -17,6 +17,17 @@ copying the scales and biases: same shapes and routing, different bytes.
 --calibrate-copy MB runs only a plain device-to-device copy of MB megabytes
 (five times); rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE over it gives the
 scale between those counters and true bytes.
+
+The pages' two ablations are timed on the 512-token workload as well
+(extra "ablation_unfused" and "ablation_host_routing"): the weights expanded to
+bf16 in memory before a GEMM over bf16 weights, and the grouping done on the
+host after a synchronising copy of the top-k.
+
+--sweep runs only the tiling and chunking sweeps and prints them as one JSON
+line: block_rows 16 / 32 / 64 (the row-block height of the block map and of
+the GEMM tiles) on the 512- and 2048-token prefill, and chunk sizes 512 /
+1024 / 2048 / 4096 of the bounded-chunk driver on the skewed 8192-token
+prefill.
 """
 from __future__ import annotations
 
@@ -58,7 +69,12 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
+    ap.add_argument("--sweep", action="store_true", help="tiling and chunking sweeps only")
     return ap.parse_args()
+
+
+def only_set(args):
+    return set(filter(None, args.only.split(",")))
 
 
 def timed(fn, steps, warmup, torch):
@@ -104,6 +120,59 @@ def calibrate_copy(mb, torch):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}))
 
 
+def host_grouping(idx, E, block_rows, max_blocks):
+    """Histogram, exclusive offsets, stable scatter and block map of the top-k
+    on the host (numpy): the host-synced routing baseline."""
+    flat = idx.reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    np.cumsum(counts, out=offsets[1:])
+    sorted_assign = np.argsort(flat, kind="stable").astype(np.int32)
+    assign_row = np.empty_like(sorted_assign)
+    assign_row[sorted_assign] = np.arange(flat.size, dtype=np.int32)
+    nb = (counts + block_rows - 1) // block_rows
+    block_expert = np.full(max_blocks, -1, np.int32)
+    block_row = np.full(max_blocks, -1, np.int32)
+    be = np.repeat(np.arange(E, dtype=np.int32), nb)
+    first = np.repeat(np.cumsum(nb) - nb, nb)
+    block_expert[:be.size] = be
+    block_row[:be.size] = offsets[be] + block_rows * (np.arange(be.size) - first)
+    return dict(counts=counts, offsets=offsets, sorted_assign=sorted_assign,
+                assign_row=assign_row, block_expert=block_expert, block_row=block_row,
+                n_blocks=np.array([be.size], np.int32))
+
+
+def sweep(args, torch, bq, dev):
+    from workload import CONFIGS, make_activations, make_weights
+    cfg = CONFIGS["prefill512"]
+    w = make_weights(cfg, seed=0)
+    base = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev)
+    mats = base.weight_mats()
+    out = {"sweep": "block_rows x prefill, chunk_tokens x skewed prefill", "unit": "tokens/s",
+           "block_rows": {}, "chunk_tokens": {}}
+    for name in ("prefill512", "prefill2048"):
+        c = CONFIGS[name]
+        xb, lgn = make_activations(c)
+        x, lg = bq.bf16_from_bits(xb, dev), torch.from_numpy(lgn).to(dev)
+        for br in (16, 32, 64):
+            L = bq.MoeLayer.from_device(mats, c.H, c.I, c.I_sh, c.E, c.k, dev, block_rows=br)
+            ms = timed(lambda: L.forward(x, lg), max(20, args.steps // 4), 5, torch)
+            out["block_rows"].setdefault(name, {})[br] = c.T / (ms * 1e-3)
+            log(f"sweep {name} block_rows {br}: {ms*1e3:.1f} us/call")
+            del L
+    c = CONFIGS["skew8192"]
+    xb, lgn = make_activations(c)
+    x, lg = bq.bf16_from_bits(xb, dev), torch.from_numpy(lgn).to(dev)
+    y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+    for chunk in (512, 1024, 2048, 4096):
+        ws = base.forward_chunked(x, lg, chunk, y)
+        ms = timed(lambda: base.forward_chunked(x, lg, chunk, y, ws), 10, 2, torch)
+        out["chunk_tokens"][chunk] = c.T / (ms * 1e-3)
+        log(f"sweep skew8192 chunk {chunk}: {ms*1e3:.1f} us per 8192 tokens")
+        del ws
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -120,6 +189,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        sweep(args, torch, bq, dev)
+        return
     cfg = CONFIGS["prefill512"]
     log("generating weights")
     w = make_weights(cfg, seed=0)
@@ -219,9 +291,50 @@ def main():
         f"gateup {t_gu*1e6:.1f} ({achieved/1e9:.0f} GB/s) down {t_dn*1e6:.1f} "
         f"combine {t_comb*1e6:.1f} us; cold {ms_cold*1e3:.1f} us/call")
 
-    # ---------------- secondary workloads ----------------
+    # ---------------- the pages' two ablations (512 tokens) ----------------
     extra = {}
-    only = set(filter(None, args.only.split(",")))
+    if not args.no_extra and (not only_set(args) or "ablations" in only_set(args)):
+        ms_unf = timed(lambda: layer.forward_unfused(x, lg), max(20, args.steps // 4), 5, torch)
+        y_fused = layer.forward(x, lg)["y"].clone()
+        y_unf = layer.forward_unfused(x, lg)["y"]
+        torch.cuda.synchronize()
+        err = float((y_unf.float() - y_fused.float()).abs().max() / y_fused.float().abs().max())
+        extra["ablation_unfused"] = {
+            "us_per_call": ms_unf * 1e3, "tokens_per_s": T / (ms_unf * 1e-3),
+            "fused_speedup": ms_unf / ms,
+            "max_rel_diff_vs_fused": err,
+            "what": "route; expand the routed and shared experts' weights to bf16 in HBM "
+                    "(moe_dequant_q4_bf16); gate/up and down GEMMs over bf16 weights; combine"}
+        log(f"ablation unfused: {ms_unf*1e3:.1f} us/call; fused is {ms_unf/ms:.2f}x faster "
+            f"(max rel diff {err:.1e})")
+        hb = layer.buffers(T)
+        hr = hb["routing"]
+        dev_arrays = {n: getattr(hr, n) for n in ("counts", "offsets", "sorted_assign",
+                                                  "assign_row", "block_expert", "block_row",
+                                                  "n_blocks")}
+
+        def host_routed():
+            bq.moe_route(lg, cfg.k, br, hr, hb["route_ws"])   # top-k (grouping redone below)
+            idx = hr.topk_idx.cpu().numpy()                  # synchronising copy
+            g = host_grouping(idx, cfg.E, br, hr.max_blocks)
+            for n, t in dev_arrays.items():
+                t.copy_(torch.from_numpy(g[n]))
+            bq.moe_grouped_gemm_q4(x, cfg.I, cfg.I_sh, cfg.E, cfg.k, br, hr, layer.gate, layer.up,
+                                   layer.down, layer.sh_gate, layer.sh_up, layer.sh_down,
+                                   hb["expert_out"], hb["shared_out"], hb["gemm_ws"])
+            bq.moe_combine(hb["expert_out"], hb["shared_out"], hr, cfg.k, hb["y"])
+        ms_host = timed(host_routed, max(20, args.steps // 4), 5, torch)
+        same = bool(torch.equal(hb["y"].view(torch.int16), y_fused.view(torch.int16)))
+        extra["ablation_host_routing"] = {
+            "us_per_call": ms_host * 1e3, "tokens_per_s": T / (ms_host * 1e-3),
+            "gpu_routing_speedup": ms_host / ms, "y_identical_to_gpu_routing": same,
+            "what": "top-k on the GPU, then a synchronising copy of topk_idx to the host, "
+                    "histogram/scan/stable scatter/block map in numpy, copies back, GEMMs, combine"}
+        log(f"ablation host routing: {ms_host*1e3:.1f} us/call; GPU-resident routing is "
+            f"{ms_host/ms:.2f}x faster (y identical: {same})")
+
+    # ---------------- secondary workloads ----------------
+    only = only_set(args)
     if not args.no_extra:
         if not only or "prefill2048" in only:
             c = CONFIGS["prefill2048"]

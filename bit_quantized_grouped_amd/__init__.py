@@ -60,6 +60,11 @@ _SIGNATURES = {
     "moe_expert_down_q4": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
                            + [ctypes.POINTER(MoeQ4Mat)] * 2 + [_P, _P, _P, _S, _P]),
     "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
+    "moe_dequant_q4_bf16": (_I, [ctypes.POINTER(MoeQ4Mat), _I, _I, _I, _P, _P, _P]),
+    "moe_expert_gateup_bf16": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
+                               + [_P] * 4 + [_P, _S, _P]),
+    "moe_expert_down_bf16": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
+                             + [_P] * 2 + [_P, _P, _P, _S, _P]),
     "moe_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_decode_q4": (_I, [_P, _P, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(MoeQ4Mat)] * 6
                       + [ctypes.POINTER(MoeRouting), _P, _P, _S, _P]),
@@ -229,6 +234,35 @@ def moe_combine(expert_out: torch.Tensor, shared_out, routing: DeviceRouting, k:
                              T, H, k, _ptr(y), _stream(stream, y.device)), "moe_combine")
 
 
+def moe_dequant_q4_bf16(m: DeviceQMat, n_exp: int, N: int, K: int, out: torch.Tensor, counts=None,
+                        stream=None):
+    """Expand a 4-bit matrix set [n_exp, N, K] into bf16 `out` [n_exp, N, K]; experts with
+    counts[e] == 0 are skipped when counts (device int32 [n_exp]) is given."""
+    _check(lib().moe_dequant_q4_bf16(ctypes.byref(m.struct), n_exp, N, K, _ptr(counts), _ptr(out),
+                                     _stream(stream, out.device)), "moe_dequant_q4_bf16")
+
+
+def moe_expert_gateup_bf16(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, block_rows: int,
+                           routing: DeviceRouting, gate, up, sh_gate, sh_up, ws: torch.Tensor,
+                           stream=None):
+    """moe_expert_gateup_q4 over bf16 weight tensors (gate/up [E, I, H], shared [1, I_sh, H])."""
+    T, H = x.shape
+    _check(lib().moe_expert_gateup_bf16(
+        _ptr(x), T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct),
+        _ptr(gate), _ptr(up), _ptr(sh_gate), _ptr(sh_up), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream, x.device)), "moe_expert_gateup_bf16")
+
+
+def moe_expert_down_bf16(T: int, H: int, I: int, I_sh: int, E: int, k: int, block_rows: int,
+                         routing: DeviceRouting, down, sh_down, expert_out: torch.Tensor, shared_out,
+                         ws: torch.Tensor, stream=None):
+    """moe_expert_down_q4 over bf16 weight tensors (down [E, H, I], shared [1, H, I_sh])."""
+    _check(lib().moe_expert_down_bf16(
+        T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct), _ptr(down), _ptr(sh_down),
+        _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream, expert_out.device)), "moe_expert_down_bf16")
+
+
 def decode_workspace_bytes(H, I, I_sh, E, k) -> int:
     return lib().moe_decode_workspace_bytes(H, I, I_sh, E, k)
 
@@ -346,6 +380,42 @@ class MoeLayer:
         moe_decode_q4(x, logits, self.I, self.I_sh, self.k, self.block_rows, *self.weight_mats(),
                       routing, y, ws, stream)
         return ws
+
+    def bf16_weights(self) -> dict:
+        """Device buffers for the weights expanded to bf16 (allocated once, reused)."""
+        if not hasattr(self, "_bf16"):
+            d, E, H, I, Is = self.device, self.E, self.H, self.I, self.I_sh
+            bf = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device=d)  # noqa: E731
+            self._bf16 = dict(gate=bf(E, I, H), up=bf(E, I, H), down=bf(E, H, I),
+                              sh_gate=bf(1, Is, H) if Is else None,
+                              sh_up=bf(1, Is, H) if Is else None,
+                              sh_down=bf(1, H, Is) if Is else None)
+        return self._bf16
+
+    def forward_unfused(self, x: torch.Tensor, logits: torch.Tensor, stream=None) -> dict:
+        """The unfused baseline: route, expand the routed experts' and the shared expert's
+        4-bit weights to bf16 in memory, then the two GEMM phases over the bf16 weights,
+        then combine; returns the buffers used."""
+        T = x.shape[0]
+        b = self.buffers(T)
+        r = b["routing"]
+        E, H, I, Is = self.E, self.H, self.I, self.I_sh
+        moe_route(logits, self.k, self.block_rows, r, b["route_ws"], stream)
+        w = self.bf16_weights()
+        for name, m, shape, counts in (("gate", self.gate, (E, I, H), r.counts),
+                                       ("up", self.up, (E, I, H), r.counts),
+                                       ("down", self.down, (E, H, I), r.counts),
+                                       ("sh_gate", self.sh_gate, (1, Is, H), None),
+                                       ("sh_up", self.sh_up, (1, Is, H), None),
+                                       ("sh_down", self.sh_down, (1, H, Is), None)):
+            if m is not None:
+                moe_dequant_q4_bf16(m, *shape, w[name], counts, stream)
+        moe_expert_gateup_bf16(x, I, Is, E, self.k, self.block_rows, r, w["gate"], w["up"],
+                               w["sh_gate"], w["sh_up"], b["gemm_ws"], stream)
+        moe_expert_down_bf16(T, H, I, Is, E, self.k, self.block_rows, r, w["down"], w["sh_down"],
+                             b["expert_out"], b["shared_out"], b["gemm_ws"], stream)
+        moe_combine(b["expert_out"], b["shared_out"], r, self.k, b["y"], stream)
+        return b
 
     def forward_chunked(self, x, logits, chunk_tokens: int, y: torch.Tensor, ws=None, stream=None):
         T = x.shape[0]

@@ -290,6 +290,84 @@ int moe_expert_down_q4(int T, int H, int I, int I_sh, int E, int k, int block_ro
     }
 }
 
+int moe_dequant_q4_bf16(const moe_q4_mat* m, int n_exp, int N, int K, const int32_t* counts,
+                        uint16_t* out, hipStream_t stream) {
+    try {
+        if (n_exp < 1 || N < 1 || K < 64 || K % 64) return MOE_ERR_SHAPE;
+        if ((size_t)n_exp * N * (K / 8) >= ((size_t)1 << 31)) return MOE_ERR_SHAPE;
+        int st = check_mat(m);
+        if (st) return st;
+        if (!out) return MOE_ERR_NULL;
+        if (!aligned(out, 16)) return MOE_ERR_ALIGN;
+        return launch_dequant_bf16(to_dev(m), n_exp, N, K, counts, out, stream) == hipSuccess
+                   ? MOE_OK
+                   : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+static int check_bf16_weights(const uint16_t* w) {
+    if (!w) return MOE_ERR_NULL;
+    return aligned(w, 16) ? MOE_OK : MOE_ERR_ALIGN;
+}
+
+int moe_expert_gateup_bf16(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
+                           int block_rows, const moe_routing* r, const uint16_t* gate,
+                           const uint16_t* up, const uint16_t* sh_gate, const uint16_t* sh_up,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+    try {
+        int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
+        if (st) return st;
+        if (!x) return MOE_ERR_NULL;
+        if ((st = check_routing(r))) return st;
+        if ((st = check_bf16_weights(gate)) || (st = check_bf16_weights(up))) return st;
+        if (I_sh) {
+            if ((st = check_bf16_weights(sh_gate)) || (st = check_bf16_weights(sh_up))) return st;
+        } else if (sh_gate || sh_up) {
+            return MOE_ERR_SHAPE;
+        }
+        if (!aligned(x, 16)) return MOE_ERR_ALIGN;
+        if ((st = check_ws(ws, ws_bytes, moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))))
+            return st;
+        const GemmProblem p = make_problem(x, T, H, I, I_sh, E, k, block_rows, r, nullptr, nullptr,
+                                           nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+        const uint16_t* const w[4] = {gate, up, sh_gate, sh_up};
+        return launch_gateup_bf16(p, w, ws, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_expert_down_bf16(int T, int H, int I, int I_sh, int E, int k, int block_rows,
+                         const moe_routing* r, const uint16_t* down, const uint16_t* sh_down,
+                         uint16_t* expert_out, uint16_t* shared_out, const void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    try {
+        int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
+        if (st) return st;
+        if (!expert_out) return MOE_ERR_NULL;
+        if ((st = check_routing(r))) return st;
+        if ((st = check_bf16_weights(down))) return st;
+        if (I_sh) {
+            if (!shared_out) return MOE_ERR_NULL;
+            if ((st = check_bf16_weights(sh_down))) return st;
+            if (!aligned(shared_out, 16)) return MOE_ERR_ALIGN;
+        } else if (sh_down || shared_out) {
+            return MOE_ERR_SHAPE;
+        }
+        if (!aligned(expert_out, 16)) return MOE_ERR_ALIGN;
+        if ((st = check_ws(ws, ws_bytes, moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))))
+            return st;
+        const GemmProblem p = make_problem(nullptr, T, H, I, I_sh, E, k, block_rows, r, nullptr,
+                                           nullptr, nullptr, nullptr, nullptr, nullptr, expert_out,
+                                           shared_out);
+        return launch_down_bf16(p, down, sh_down, ws, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
 int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const moe_routing* r,
                 int T, int H, int k, uint16_t* y, hipStream_t stream) {
     try {

@@ -91,6 +91,8 @@ struct GroupedArgs {
     const int32_t* offsets;
     int sh_blocks;
     QMatDev rB[2];
+    const uint16_t* rW[2];          // bf16-weight mode: routed weights [E, N, K]
+    const uint16_t* sW[2];          // bf16-weight mode: shared weights [1, N_sh, K_sh]
     QMatDev sB[2];
     int N, K, N_sh, K_sh;
     int n_tiles;                    // column tiles per row block (of the wider of N, N_sh)
@@ -105,10 +107,13 @@ struct GroupedArgs {
 // consecutive blocks of one expert, then share an L2.
 constexpr int kXcds = 8;
 
-template <int NMAT, int NSUB, int W>
+// One K-chunk of a lane's B operand: W code words per weight row (4-bit
+// weights), or, in the bf16-weight mode (BF), W x 8 bf16 weights per row.
+template <int NMAT, int NSUB, int W, bool BF = false>
 struct BChunk {
     u32x4_t w[NMAT][NSUB][W / 4 > 0 ? W / 4 : 1];
     u32x2_t w2[NMAT][NSUB];           // used when W == 2
+    u32x4_t wb[NMAT][NSUB][BF ? W : 1];
 };
 
 template <int NMAT, int NSUB, int KC>
@@ -126,14 +131,23 @@ struct Streams {
 // loads it waits for all of them once per pass over the register ring).
 constexpr int kVoffOob = 0x40000000;
 
-template <int NMAT, int NSUB, int KC>
-__device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32>& B,
+template <int NMAT, int NSUB, int KC, bool BF>
+__device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                        const Streams<NMAT, NSUB, KC>& S, int c, int voff_oob) {
     constexpr int W = KC / 32;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
+            if constexpr (BF) {   // bf16 rows: K * 2 bytes; a chunk is KC * 2 bytes of a row
+                const int so_b = s * S.sub_c + c * (KC * 2);
+#pragma unroll
+                for (int j = 0; j < W; ++j)
+                    B.wb[m][s][j] = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                     S.codes[m], S.voff_c + voff_oob + 16 * j, so_b, 0));
+                continue;
+            }
             const int so_c = s * S.sub_c + c * (KC / 2);
             if constexpr (W >= 4) {
 #pragma unroll
@@ -149,16 +163,16 @@ __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32>& B,
         }
 }
 
-template <int NMAT, int NSUB, int W>
-__device__ __forceinline__ uint32_t word_of(const BChunk<NMAT, NSUB, W>& B, int m, int s, int j) {
+template <int NMAT, int NSUB, int W, bool BF>
+__device__ __forceinline__ uint32_t word_of(const BChunk<NMAT, NSUB, W, BF>& B, int m, int s, int j) {
     if constexpr (W >= 4) return B.w[m][s][j / 4][j % 4];
     else return B.w2[m][s][j];
 }
 
 // sSc / sBi: this lane's row of bf16 scales / biases in LDS (row stride GS,
 // matrix stride mstride); grp = the group of the lane's words in this chunk.
-template <int NMAT, int MT, int KC, int NSUB>
-__device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32>& B,
+template <int NMAT, int MT, int KC, int NSUB, bool BF>
+__device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                               const uint16_t* sAc, const uint16_t* sSc,
                                               const uint16_t* sBi, int GS, int mstride, int grp,
                                               float unit_inv, int nl, int g, int msub_act,
@@ -170,6 +184,7 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32>&
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
+            if constexpr (BF) break;
             const int at = m * mstride + s * 16 * GS + grp;
             sc[m][s] = bf16_to_f32(sSc[at]) * unit_inv;
             bi[m][s] = bf16_to_f32(sBi[at]);
@@ -181,7 +196,8 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32>&
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
-                bw[m][s] = dequant_word(word_of(B, m, s, j), sc[m][s], bi[m][s]);
+                if constexpr (BF) bw[m][s] = __builtin_bit_cast(bf16x8_t, B.wb[m][s][j]);
+                else bw[m][s] = dequant_word(word_of(B, m, s, j), sc[m][s], bi[m][s]);
 #pragma unroll
         for (int mi = 0; mi < MT / 16; ++mi) {
             if (mi > 0 && mi >= msub_act) break;   // 16-row subtiles past the block's rows
@@ -195,7 +211,9 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32>&
     }
 }
 
-template <int NMAT, int MT, int KC, int NSUB, int DEPTH, int WAVES>
+// BF: the weights are plain bf16 [n_exp, N, K] (rW / sW), already expanded
+// in memory; the unfused layout the pages compare against.
+template <int NMAT, int MT, int KC, int NSUB, int DEPTH, int WAVES, bool BF = false>
 __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     constexpr int NT = WAVES * 64;   // threads
     constexpr int W = KC / 32;       // code words per lane per chunk
@@ -266,8 +284,12 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     Streams<NMAT, NSUB, KC> S;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-        const QMatDev& q = is_sh ? p.sB[m] : p.rB[m];
         const size_t rows0 = (size_t)expert * N;
+        if constexpr (BF) {   // expanded bf16 weights: no scales
+            S.codes[m] = make_rsrc((is_sh ? p.sW[m] : p.rW[m]) + rows0 * K, (uint32_t)N * K * 2);
+            continue;
+        }
+        const QMatDev& q = is_sh ? p.sB[m] : p.rB[m];
         S.codes[m] = make_rsrc(q.codes + rows0 * (K / 8), (uint32_t)N * (K / 2));
         const rsrc_t rs_s = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
         const rsrc_t rs_b = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
@@ -294,8 +316,13 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         }
     }
     const int row_lane = wave * NSUB * 16 + nl;     // lane's row within the tile
-    S.voff_c = (n_base + row_lane) * (K / 2) + g * W * 4;
-    S.sub_c = 16 * (K / 2);
+    if constexpr (BF) {
+        S.voff_c = (n_base + row_lane) * (K * 2) + g * W * 16;
+        S.sub_c = 16 * (K * 2);
+    } else {
+        S.voff_c = (n_base + row_lane) * (K / 2) + g * W * 4;
+        S.sub_c = 16 * (K / 2);
+    }
     const int lane_grp = (g * (KC / 4)) / 64;
     const uint16_t* sSc_lane = sSc + row_lane * GS + lane_grp;
     const uint16_t* sBi_lane = sBi + row_lane * GS + lane_grp;
@@ -345,7 +372,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     // chunk's math, so no load latency sits between two barriers.  A chunk c
     // is staged into LDS buffer c % 2 one chunk ahead of its math.  Requests
     // past the last chunk go out of bounds (kVoffOob) and are never used.
-    BChunk<NMAT, NSUB, W> Bq[DEPTH];
+    BChunk<NMAT, NSUB, W, BF> Bq[DEPTH];
     u32x4_t Aq[DEPTH][APT];
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) {
@@ -431,11 +458,11 @@ static int pick_kc(int K, int K2, int kc_max) {
     return 0;
 }
 
-template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES>
+template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES, bool BF>
 static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_cu,
                       hipStream_t stream) {
 #define MOE_LAUNCH(KCV)                                                                          \
-    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES><<<                                      \
+    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES, BF><<<                                  \
         grid, WAVES * 64, grouped_lds_bytes<NMAT, MT, KCV, NSUB, WAVES>(G, wg_per_cu), stream>>>(a)
     if (kc == 256) MOE_LAUNCH(256);
     else if (kc == 128) MOE_LAUNCH(128);
@@ -443,16 +470,16 @@ static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_
 #undef MOE_LAUNCH
 }
 
-template <int NMAT, int NSUB, int DEPTH, int WAVES>
+template <int NMAT, int NSUB, int DEPTH, int WAVES, bool BF = false>
 static void launch_grouped(GroupedArgs a, int mt, int kc, int n_max, int slots, int G,
                            int wg_per_cu, hipStream_t stream) {
     constexpr int cols = WAVES * NSUB * 16;
     a.n_tiles = (n_max + cols - 1) / cols;
     const long long items = (long long)slots * a.n_tiles;
     const int grid = (int)((items + kXcds - 1) / kXcds) * kXcds;
-    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES>(a, kc, grid, G, wg_per_cu, stream);
-    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES>(a, kc, grid, G, wg_per_cu, stream);
-    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES>(a, kc, grid, G, wg_per_cu, stream);
+    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES, BF>(a, kc, grid, G, wg_per_cu, stream);
+    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES, BF>(a, kc, grid, G, wg_per_cu, stream);
+    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES, BF>(a, kc, grid, G, wg_per_cu, stream);
 }
 
 static GroupedArgs common_args(const GemmProblem& p) {
@@ -469,11 +496,10 @@ static GroupedArgs common_args(const GemmProblem& p) {
 }
 
 // gate + up with SwiGLU: A = x (gathered by token), N = I, K = H -> h in ws
-hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
+static GroupedArgs gateup_args(const GemmProblem& p, void* ws) {
     size_t off_h, off_hsh;
     gemm_ws_layout(p.T, p.I, p.I_sh, p.k, &off_h, &off_hsh);
     GroupedArgs a = common_args(p);
-    const int slots = a.sh_blocks + p.max_blocks;
     a.a_routed = p.x;
     a.a_shared = p.x;
     a.lda_routed = a.lda_shared = p.H;
@@ -489,18 +515,14 @@ hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
     a.K_sh = p.H;
     a.out_routed = (uint16_t*)((char*)ws + off_h);
     a.out_shared = (uint16_t*)((char*)ws + off_hsh);
-    launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES>(
-        a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh, slots, p.H / 64,
-        MOE_GU_WG_PER_CU, stream);
-    return hipGetLastError();
+    return a;
 }
 
 // down: A = h rows (contiguous, from ws), N = H, K = I -> expert_out / shared_out
-hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream) {
+static GroupedArgs down_args(const GemmProblem& p, const void* ws) {
     size_t off_h, off_hsh;
     gemm_ws_layout(p.T, p.I, p.I_sh, p.k, &off_h, &off_hsh);
     GroupedArgs a = common_args(p);
-    const int slots = a.sh_blocks + p.max_blocks;
     a.a_routed = (const uint16_t*)((const char*)ws + off_h);
     a.a_shared = (const uint16_t*)((const char*)ws + off_hsh);
     a.lda_routed = p.I;
@@ -516,8 +538,50 @@ hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream)
     a.K_sh = p.I_sh;
     a.out_routed = p.expert_out;
     a.out_shared = p.shared_out;
+    return a;
+}
+
+hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
+    const GroupedArgs a = gateup_args(p, ws);
+    launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES>(
+        a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
+        a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream) {
+    const GroupedArgs a = down_args(p, ws);
     launch_grouped<1, MOE_DN_NSUB, MOE_DN_DEPTH, MOE_DN_WAVES>(
-        a, p.block_rows, pick_kc(p.I, p.I_sh, MOE_DN_KC), p.H, slots,
+        a, p.block_rows, pick_kc(p.I, p.I_sh, MOE_DN_KC), p.H, a.sh_blocks + p.max_blocks,
+        (p.I > p.I_sh ? p.I : p.I_sh) / 64, MOE_DN_WG_PER_CU, stream);
+    return hipGetLastError();
+}
+
+// The same two phases over weights already expanded to bf16 in memory (the
+// unfused baseline).  A bf16 chunk is 4x the bytes of a 4-bit one, so the
+// K-chunk is halved to keep the register ring the same size.
+constexpr int kBfKc = 64;
+
+hipError_t launch_gateup_bf16(const GemmProblem& p, const uint16_t* const w[4], void* ws,
+                              hipStream_t stream) {
+    GroupedArgs a = gateup_args(p, ws);
+    a.rW[0] = w[0];
+    a.rW[1] = w[1];
+    a.sW[0] = w[2];
+    a.sW[1] = w[3];
+    launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES, true>(
+        a, p.block_rows, pick_kc(p.H, 0, kBfKc), p.I > p.I_sh ? p.I : p.I_sh,
+        a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_bf16(const GemmProblem& p, const uint16_t* down, const uint16_t* sh_down,
+                            const void* ws, hipStream_t stream) {
+    GroupedArgs a = down_args(p, ws);
+    a.rW[0] = down;
+    a.sW[0] = sh_down;
+    launch_grouped<1, MOE_DN_NSUB, MOE_DN_DEPTH, MOE_DN_WAVES, true>(
+        a, p.block_rows, pick_kc(p.I, p.I_sh, kBfKc), p.H, a.sh_blocks + p.max_blocks,
         (p.I > p.I_sh ? p.I : p.I_sh) / 64, MOE_DN_WG_PER_CU, stream);
     return hipGetLastError();
 }

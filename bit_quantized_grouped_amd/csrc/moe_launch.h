@@ -46,6 +46,15 @@ struct GemmProblem {
 size_t gemm_ws_layout(int T, int I, int I_sh, int k, size_t* off_h, size_t* off_hsh);
 hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream);
+// weights expanded to bf16 [n_exp, N, K]: w = {gate, up, shared gate, shared up}
+hipError_t launch_gateup_bf16(const GemmProblem& p, const uint16_t* const w[4], void* ws,
+                              hipStream_t stream);
+hipError_t launch_down_bf16(const GemmProblem& p, const uint16_t* down, const uint16_t* sh_down,
+                            const void* ws, hipStream_t stream);
+
+// dequant.hip
+hipError_t launch_dequant_bf16(const QMatDev& m, int n_exp, int N, int K, const int32_t* counts,
+                               uint16_t* out, hipStream_t stream);
 
 // decode.hip
 struct DecodeArgs {

@@ -167,6 +167,34 @@ int moe_expert_down_q4(int T, int H, int I, int I_sh, int E, int k, int block_ro
                        uint16_t* expert_out, uint16_t* shared_out,
                        const void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Unfused baseline ([P2] aikraft.ru, "Technical optimizations: Prefill
+ * and Decode"; [P3] droneth.or.th, ablation paragraph: the pages measure the
+ * fused grouped GEMM against expanding the weights first). ---- */
+
+/* Expand a 4-bit matrix set [n_exp, N, K] to bf16 [n_exp, N, K] (uint16 bit
+ * patterns) in `out`, with the same arithmetic as the fused GEMM:
+ * w = bf16_rne(fp32(q * scale + bias)).  counts: device int32 [n_exp] or
+ * NULL; when given, experts with counts[e] == 0 are skipped and their rows of
+ * `out` are left as they were.  out: n_exp*N*K*2 bytes, 16-byte aligned,
+ * caller-owned.  K a multiple of 64, n_exp*N*K/8 < 2^31.  Enqueues one kernel. */
+int moe_dequant_q4_bf16(const moe_q4_mat* m, int n_exp, int N, int K, const int32_t* counts,
+                        uint16_t* out, hipStream_t stream);
+
+/* moe_expert_gateup_q4 / moe_expert_down_q4 over weights already expanded to
+ * bf16 (e.g. by moe_dequant_q4_bf16): gate/up bf16 [E, I, H], shared [1, I_sh, H],
+ * down bf16 [E, H, I], shared [1, H, I_sh], each 16-byte aligned.  Same
+ * routing, workspace and outputs as the 4-bit entry points; the GEMM tiles
+ * and pipeline are the same, only the weight operand is read as bf16. */
+int moe_expert_gateup_bf16(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
+                           int block_rows, const moe_routing* r, const uint16_t* gate,
+                           const uint16_t* up, const uint16_t* sh_gate, const uint16_t* sh_up,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+int moe_expert_down_bf16(int T, int H, int I, int I_sh, int E, int k, int block_rows,
+                         const moe_routing* r, const uint16_t* down, const uint16_t* sh_down,
+                         uint16_t* expert_out, uint16_t* shared_out, const void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
 /* Weighted combine: y[t] = sum_j topk_w[t,j] * expert_out[assign_row[t*k+j]]
  * + shared_out[t], summed in fp32 in slot order with the shared expert last
  * (weight 1; the pages name no shared-expert gate), rounded once to bf16.

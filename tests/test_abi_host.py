@@ -162,3 +162,34 @@ def test_decode_rejects_bad_arguments():
     assert call(r=ctypes.byref(bad)) == bq.MOE_ERR_NULL
     assert L.moe_decode_q4_sequential(FAKE, FAKE, 0, 2048, 512, 512, 256, 8, *mats, FAKE, FAKE,
                                       ws, None) == bq.MOE_ERR_SHAPE
+
+
+def test_unfused_baseline_rejects_bad_arguments():
+    L = bq.lib()
+    m = _mat()
+    dq = lambda mat=m, n=4, N=64, K=128, out=FAKE: L.moe_dequant_q4_bf16(  # noqa: E731
+        ctypes.byref(mat) if mat is not None else None, n, N, K, None, out, None)
+    assert dq(mat=None) == bq.MOE_ERR_NULL
+    assert dq(out=None) == bq.MOE_ERR_NULL
+    assert dq(K=100) == bq.MOE_ERR_SHAPE
+    assert dq(n=0) == bq.MOE_ERR_SHAPE
+    assert dq(n=1 << 12, N=1 << 12, K=1 << 12) == bq.MOE_ERR_SHAPE    # 2^33 words
+    assert dq(out=MISALIGNED) == bq.MOE_ERR_ALIGN
+    assert dq(mat=_mat(MISALIGNED)) == bq.MOE_ERR_ALIGN
+    r = _routing()
+    ws = bq.gemm_workspace_bytes(64, 256, 128, 128, 16, 2, 32)
+    gu = lambda x=FAKE, w=FAKE, sh=FAKE, I_sh=128, wsb=ws: L.moe_expert_gateup_bf16(  # noqa: E731
+        x, 64, 256, 128, I_sh, 16, 2, 32, ctypes.byref(r), w, FAKE, sh, sh, FAKE, wsb, None)
+    assert gu(x=None) == bq.MOE_ERR_NULL
+    assert gu(w=None) == bq.MOE_ERR_NULL
+    assert gu(w=MISALIGNED) == bq.MOE_ERR_ALIGN
+    assert gu(sh=None) == bq.MOE_ERR_NULL                      # I_sh > 0 needs shared weights
+    assert gu(I_sh=0) == bq.MOE_ERR_SHAPE                      # shared weights without I_sh
+    assert gu(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
+    dn = lambda eo=FAKE, so=FAKE, w=FAKE, I_sh=128: L.moe_expert_down_bf16(  # noqa: E731
+        64, 256, 128, I_sh, 16, 2, 32, ctypes.byref(r), w, FAKE if I_sh else None, eo, so, FAKE, ws,
+        None)
+    assert dn(eo=None) == bq.MOE_ERR_NULL
+    assert dn(so=None) == bq.MOE_ERR_NULL
+    assert dn(w=MISALIGNED) == bq.MOE_ERR_ALIGN
+    assert dn(I_sh=0) == bq.MOE_ERR_SHAPE                      # shared_out without I_sh
