@@ -7,4 +7,5 @@ docstring and in the pins under tests/ (test_oracle_*.py).
 from .moe_oracle import (  # noqa: F401
     bf16_bits_to_f64, f32_to_bf16_rne_bits, unpack_codes, dequant_bf16_bits, dequant,
     route_topk, max_blocks, group, silu, swiglu_ffn, moe_layer, moe_layer_chunked,
+    router_logits, shared_gate,
 )

@@ -30,9 +30,13 @@ reports on Perplexity's "Lily" engine:
   ([P1] tiling bullet, 16 -> 32-row tiles).
 * Each expert is a SwiGLU FFN (silu(x Wg^T) * (x Wu^T)) Wd^T with no biases;
   the layer output is the routing-weighted sum of the k expert outputs plus
-  the shared expert's output with weight 1.
+  the shared expert's output with weight 1 (unless the optional gate is on).
 * Long prompts run in bounded chunks ([P1] "Prefill optimizations", memory
   bullet): each chunk is an independent layer call.
+* The router's scores are a plain projection of the token's activations,
+  logits = x W_r^T in fp64 ([P1] "Model specification"); an optional
+  per-token shared-expert weight sigmoid(x . w_g) (not named by the pages,
+  off unless asked) scales the shared expert's output.
 
 Readings taken where the pages are silent are listed in the design notes of
 the repository; every one of them is applied here and nowhere else.
@@ -182,6 +186,21 @@ def group(idx: np.ndarray, E: int, block_rows: int = 32) -> dict:
 # Expert FFN and combine
 # ----------------------------------------------------------------------------
 
+def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
+    """Router scores ([P1] "Model specification": a router scores the 256
+    experts for every token): logits[t, e] = sum_h x[t, h] * W_r[e, h], with
+    x bf16 [T, H] and W_r bf16 [E, H] (uint16 bit patterns), in fp64."""
+    return bf16_bits_to_f64(x_bits) @ bf16_bits_to_f64(wr_bits).T
+
+
+def shared_gate(x_bits: np.ndarray, wg_bits: np.ndarray) -> np.ndarray:
+    """Optional per-token weight of the shared expert, g[t] = sigmoid(x[t] . w_g)
+    (w_g bf16 [H]), in fp64.  The pages name no such gate (the shared expert
+    sees every token); this is the common sigmoid-gated form, off unless asked."""
+    z = bf16_bits_to_f64(x_bits) @ bf16_bits_to_f64(wg_bits)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 def silu(z: np.ndarray) -> np.ndarray:
     """z * sigmoid(z) in fp64."""
     return z / (1.0 + np.exp(-z))
@@ -199,15 +218,18 @@ def _mat(m, e: int):
 
 
 def moe_layer(x_bits: np.ndarray, logits: np.ndarray, gate, up, down, k: int,
-              sh_gate=None, sh_up=None, sh_down=None, block_rows: int = 32) -> dict:
+              sh_gate=None, sh_up=None, sh_down=None, block_rows: int = 32,
+              shared_w=None) -> dict:
     """One layer call over T tokens.
 
     x_bits: uint16 [T, H] bf16 activations; logits: float32 [T, E].
     gate/up: objects with .codes [E, I, H/8], .scales/.biases [E, I, H/64];
     down: .codes [E, H, I/8], .scales/.biases [E, H, I/64]; shared matrices
     likewise with one expert.
+    shared_w: optional fp64 [T] weight of the shared expert per token (default 1).
     Returns dict with routing arrays, topk_w, expert_out (fp64 [T*k, H],
-    sorted-row order, unweighted), shared_out (fp64 [T, H]) and y (fp64 [T, H]).
+    sorted-row order, unweighted), shared_out (fp64 [T, H], unweighted) and
+    y (fp64 [T, H]).
     """
     x = bf16_bits_to_f64(x_bits)
     T, H = x.shape
@@ -227,7 +249,7 @@ def moe_layer(x_bits: np.ndarray, logits: np.ndarray, gate, up, down, k: int,
     y = np.zeros((T, H))
     for j in range(k):
         y += w[:, j:j + 1] * expert_out[g["assign_row"][np.arange(T) * k + j]]
-    y += shared_out
+    y += shared_out if shared_w is None else np.asarray(shared_w)[:, None] * shared_out
     out = dict(topk_idx=idx, topk_w=w, expert_out=expert_out, shared_out=shared_out, y=y)
     out.update(g)
     return out
