@@ -61,6 +61,8 @@ _SIGNATURES = {
                            + [ctypes.POINTER(MoeQ4Mat)] * 2 + [_P, _P, _P, _S, _P]),
     "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
     "moe_dequant_q4_bf16": (_I, [ctypes.POINTER(MoeQ4Mat), _I, _I, _I, _P, _P, _P]),
+    "moe_combine_gated": (_I, [_P, _P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
+    "moe_router": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P]),
     "moe_expert_gateup_bf16": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
                                + [_P] * 4 + [_P, _S, _P]),
     "moe_expert_down_bf16": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
@@ -261,6 +263,25 @@ def moe_expert_down_bf16(T: int, H: int, I: int, I_sh: int, E: int, k: int, bloc
         T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct), _ptr(down), _ptr(sh_down),
         _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, expert_out.device)), "moe_expert_down_bf16")
+
+
+def moe_combine_gated(expert_out: torch.Tensor, shared_out: torch.Tensor, shared_gate: torch.Tensor,
+                      routing: DeviceRouting, k: int, y: torch.Tensor, stream=None):
+    """moe_combine with the shared expert weighted per token by shared_gate (fp32 [T])."""
+    T, H = y.shape
+    _check(lib().moe_combine_gated(_ptr(expert_out), _ptr(shared_out), _ptr(shared_gate),
+                                   ctypes.byref(routing.struct), T, H, k, _ptr(y),
+                                   _stream(stream, y.device)), "moe_combine_gated")
+
+
+def moe_router(x: torch.Tensor, w_router: torch.Tensor, logits: torch.Tensor, w_gate=None,
+               gate=None, stream=None):
+    """logits [T, E] (fp32) = x [T, H] (bf16) @ w_router [E, H]^T; optionally
+    gate [T] = sigmoid(x @ w_gate)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check(lib().moe_router(_ptr(x), T, H, _ptr(w_router), E, _ptr(w_gate), _ptr(logits),
+                            _ptr(gate), _stream(stream, x.device)), "moe_router")
 
 
 def decode_workspace_bytes(H, I, I_sh, E, k) -> int:

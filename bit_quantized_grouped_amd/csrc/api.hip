@@ -377,8 +377,44 @@ int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const mo
         if (!aligned(expert_out, 16) || !aligned(y, 16) || (shared_out && !aligned(shared_out, 16)))
             return MOE_ERR_ALIGN;
         const hipError_t e =
-            launch_combine(expert_out, shared_out, r->assign_row, r->topk_w, T, H, k, y, stream);
+            launch_combine(expert_out, shared_out, nullptr, r->assign_row, r->topk_w, T, H, k, y, stream);
         return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_combine_gated(const uint16_t* expert_out, const uint16_t* shared_out,
+                      const float* shared_gate, const moe_routing* r, int T, int H, int k,
+                      uint16_t* y, hipStream_t stream) {
+    try {
+        if (T < 1 || k < 1 || H < 64 || H % 64) return MOE_ERR_SHAPE;
+        if ((long long)T * k * H >= (1ll << 31)) return MOE_ERR_SHAPE;
+        if (!expert_out || !shared_out || !shared_gate || !y || !r || !r->assign_row || !r->topk_w)
+            return MOE_ERR_NULL;
+        if (!aligned(expert_out, 16) || !aligned(y, 16) || !aligned(shared_out, 16) ||
+            !aligned(shared_gate, 4))
+            return MOE_ERR_ALIGN;
+        const hipError_t e = launch_combine(expert_out, shared_out, shared_gate, r->assign_row,
+                                            r->topk_w, T, H, k, y, stream);
+        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
+               const uint16_t* w_gate, float* logits, float* gate, hipStream_t stream) {
+    try {
+        if (T < 1 || H < 64 || H % 64 || E < 1 || E > 1000) return MOE_ERR_SHAPE;
+        if (!x || !w_router || !logits) return MOE_ERR_NULL;
+        if ((w_gate == nullptr) != (gate == nullptr)) return MOE_ERR_NULL;
+        if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(logits, 4) ||
+            (w_gate && !aligned(w_gate, 16)) || (gate && !aligned(gate, 4)))
+            return MOE_ERR_ALIGN;
+        return launch_router(x, T, H, w_router, E, w_gate, logits, gate, stream) == hipSuccess
+                   ? MOE_OK
+                   : MOE_ERR_HIP;
     } catch (...) {
         return MOE_ERR_HIP;
     }

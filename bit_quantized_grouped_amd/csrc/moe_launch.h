@@ -76,7 +76,11 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream);
 
 // combine.hip
 hipError_t launch_combine(const uint16_t* expert_out, const uint16_t* shared_out,
-                          const int32_t* assign_row, const float* topk_w, int T, int H, int k,
-                          uint16_t* y, hipStream_t stream);
+                          const float* shared_w, const int32_t* assign_row, const float* topk_w,
+                          int T, int H, int k, uint16_t* y, hipStream_t stream);
+
+// router.hip
+hipError_t launch_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
+                         const uint16_t* w_gate, float* logits, float* gate, hipStream_t stream);
 
 }  // namespace moeq4

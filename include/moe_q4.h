@@ -202,6 +202,28 @@ int moe_expert_down_bf16(int T, int H, int I, int I_sh, int E, int k, int block_
 int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const moe_routing* r,
                 int T, int H, int k, uint16_t* y, hipStream_t stream);
 
+/* Weighted combine with a per-token weight on the shared expert:
+ * y[t] = sum_j topk_w[t,j] * expert_out[assign_row[t*k+j]] + shared_gate[t] * shared_out[t],
+ * fp32 sums in slot order, shared last, one bf16 rounding.  The pages name no
+ * gate for the shared expert (moe_combine uses weight 1); this entry serves
+ * models that gate it, e.g. with the gate output of moe_router.
+ *   shared_gate: fp32 [T] device, 4-byte aligned; other arguments as moe_combine,
+ *   except that shared_out is required. */
+int moe_combine_gated(const uint16_t* expert_out, const uint16_t* shared_out,
+                      const float* shared_gate, const moe_routing* r, int T, int H, int k,
+                      uint16_t* y, hipStream_t stream);
+
+/* Router projection ([P1] dothoosh.com, "Model specification": a router
+ * scores the 256 experts of every token): the logits moe_route selects on.
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h]  (bf16 in, fp32 accumulation)
+ *   gate[t] = sigmoid(sum_h x[t, h] * w_gate[h])    (only when w_gate is given)
+ * x bf16 [T, H], w_router bf16 [E, H], w_gate bf16 [H] (each 16-byte aligned);
+ * logits fp32 [T, E] row-major, gate fp32 [T] (4-byte aligned), caller-owned.
+ * w_gate and gate are both given or both NULL.  H a multiple of 64,
+ * 1 <= E <= 1000.  Enqueues one kernel. */
+int moe_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
+               const uint16_t* w_gate, float* logits, float* gate, hipStream_t stream);
+
 /* Device workspace bytes moe_decode_q4 needs (0 on bad shapes). */
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k);
 

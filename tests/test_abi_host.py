@@ -193,3 +193,26 @@ def test_unfused_baseline_rejects_bad_arguments():
     assert dn(so=None) == bq.MOE_ERR_NULL
     assert dn(w=MISALIGNED) == bq.MOE_ERR_ALIGN
     assert dn(I_sh=0) == bq.MOE_ERR_SHAPE                      # shared_out without I_sh
+
+
+def test_router_and_gated_combine_reject_bad_arguments():
+    L = bq.lib()
+    rt = lambda x=FAKE, T=16, H=256, wr=FAKE, E=64, wg=None, lg=FAKE, g=None: L.moe_router(  # noqa: E731
+        x, T, H, wr, E, wg, lg, g, None)
+    assert rt(x=None) == bq.MOE_ERR_NULL
+    assert rt(lg=None) == bq.MOE_ERR_NULL
+    assert rt(wg=FAKE) == bq.MOE_ERR_NULL          # gate row without a gate output
+    assert rt(g=FAKE) == bq.MOE_ERR_NULL           # gate output without a gate row
+    assert rt(H=100) == bq.MOE_ERR_SHAPE
+    assert rt(E=0) == bq.MOE_ERR_SHAPE
+    assert rt(E=1001) == bq.MOE_ERR_SHAPE
+    assert rt(T=0) == bq.MOE_ERR_SHAPE
+    assert rt(x=MISALIGNED) == bq.MOE_ERR_ALIGN
+    assert rt(wg=MISALIGNED, g=FAKE) == bq.MOE_ERR_ALIGN
+    r = _routing()
+    cg = lambda so=FAKE, g=FAKE, y=FAKE: L.moe_combine_gated(  # noqa: E731
+        FAKE, so, g, ctypes.byref(r), 8, 256, 2, y, None)
+    assert cg(so=None) == bq.MOE_ERR_NULL
+    assert cg(g=None) == bq.MOE_ERR_NULL
+    assert cg(g=P(0x10002)) == bq.MOE_ERR_ALIGN
+    assert cg(y=MISALIGNED) == bq.MOE_ERR_ALIGN

@@ -148,6 +148,17 @@ def make_weights(cfg: LayerConfig, seed: int = 0, cache: bool = True) -> LayerWe
     return w
 
 
+def make_router(cfg: LayerConfig, seed: int = 100):
+    """Router weights bf16 [E, H] and a shared-expert gate row bf16 [H] (uint16
+    bit patterns), drawn N(0, 1/H) with default_rng(seed) so that router
+    logits over N(0, 1) activations are about N(0, 1) like the drawn logits."""
+    rng = np.random.default_rng(seed)
+    scale = np.float32(1.0 / np.sqrt(cfg.H))
+    wr = f32_to_bf16_bits(rng.standard_normal((cfg.E, cfg.H), dtype=np.float32) * scale)
+    wg = f32_to_bf16_bits(rng.standard_normal(cfg.H, dtype=np.float32) * scale)
+    return wr, wg
+
+
 def zipf_bias(E: int, s: float, perm: np.ndarray) -> np.ndarray:
     """Per-expert log-popularity bias: expert perm[i] gets rank i+1 and bias -s*ln(rank)."""
     rank = np.empty(E, np.int64)
