@@ -333,6 +333,22 @@ def main():
         log(f"ablation host routing: {ms_host*1e3:.1f} us/call; GPU-resident routing is "
             f"{ms_host/ms:.2f}x faster (y identical: {same})")
 
+    # ---------------- router projection (the input of routing) ----------------
+    if not args.no_extra and (not only_set(args) or "router" in only_set(args)):
+        from workload import make_router
+        wr_bits, wg_bits = make_router(cfg)
+        wr, wg = bq.bf16_from_bits(wr_bits, dev), bq.bf16_from_bits(wg_bits, dev)
+        lg_r = torch.empty((T, cfg.E), dtype=torch.float32, device=dev)
+        g_r = torch.empty(T, dtype=torch.float32, device=dev)
+        ms_r = timed(lambda: bq.moe_router(x, wr, lg_r, wg, g_r), args.steps, args.warmup, torch)
+        ms_r1 = timed(lambda: bq.moe_router(x[:1], wr, lg_r[:1], wg, g_r[:1]), args.steps,
+                      args.warmup, torch)
+        r_bytes = T * cfg.H * 2 + (cfg.E + 1) * cfg.H * 2 + T * (cfg.E + 1) * 4
+        extra["router"] = {"us_512": ms_r * 1e3, "us_1": ms_r1 * 1e3,
+                           "hbm_frac_512": r_bytes / (ms_r * 1e-3) / HBM_PEAK,
+                           "what": "logits = x W_r^T for 256 experts plus the shared-expert gate row"}
+        log(f"router: {ms_r*1e3:.1f} us at 512 tokens, {ms_r1*1e3:.1f} us at 1 token")
+
     # ---------------- secondary workloads ----------------
     only = only_set(args)
     if not args.no_extra:
