@@ -340,9 +340,19 @@ def main():
         wr, wg = bq.bf16_from_bits(wr_bits, dev), bq.bf16_from_bits(wg_bits, dev)
         lg_r = torch.empty((T, cfg.E), dtype=torch.float32, device=dev)
         g_r = torch.empty(T, dtype=torch.float32, device=dev)
-        ms_r = timed(lambda: bq.moe_router(x, wr, lg_r, wg, g_r), args.steps, args.warmup, torch)
-        ms_r1 = timed(lambda: bq.moe_router(x[:1], wr, lg_r[:1], wg, g_r[:1]), args.steps,
-                      args.warmup, torch)
+        def graphed(fn, n=20):
+            # n calls captured once, so the host's per-call cost does not pace the GPU
+            fn()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(n):
+                    fn()
+            ms_ = timed(gr.replay, 10, 2, torch) / n
+            del gr
+            return ms_
+        ms_r = graphed(lambda: bq.moe_router(x, wr, lg_r, wg, g_r))
+        ms_r1 = graphed(lambda: bq.moe_router(x[:1], wr, lg_r[:1], wg, g_r[:1]))
         r_bytes = T * cfg.H * 2 + (cfg.E + 1) * cfg.H * 2 + T * (cfg.E + 1) * 4
         extra["router"] = {"us_512": ms_r * 1e3, "us_1": ms_r1 * 1e3,
                            "hbm_frac_512": r_bytes / (ms_r * 1e-3) / HBM_PEAK,

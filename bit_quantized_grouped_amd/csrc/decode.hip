@@ -36,8 +36,14 @@ namespace moeq4 {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / WAVE;
 constexpr int kDecMaxK = 64;
-constexpr int kGuRows = 4;    // gate/up row pairs one wave streams together
-constexpr int kDnExp = 3;     // experts whose down rows one wave loads together
+#ifndef MOE_DEC_GU_ROWS
+#define MOE_DEC_GU_ROWS 2
+#endif
+#ifndef MOE_DEC_DN_EXP
+#define MOE_DEC_DN_EXP 1
+#endif
+constexpr int kGuRows = MOE_DEC_GU_ROWS;   // gate/up row pairs one wave streams together
+constexpr int kDnExp = MOE_DEC_DN_EXP;     // experts whose down rows one wave loads together
 constexpr int kDnCols = 4;    // output columns per down workgroup (16 lanes each)
 
 // q * 2^-9 for the 8 codes of a packed word, in code order (low nibble first).
@@ -207,11 +213,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
                                                   __builtin_fmaf(bu[r], sx, acc[kGuRows + r]));
             }
         }
-        // lane l < 32 now holds g of row (l >> 3) & 3 and lane l + 32 holds u of that row
+        // value i (g of row i, then u of row i - kGuRows) ends in lanes
+        // [i * kLanesPerVal, (i + 1) * kLanesPerVal): lane l < 32 holds g of row
+        // l / kLanesPerVal and lane l + 32 holds u of that row
+        constexpr int kLanesPerVal = WAVE / (2 * kGuRows);
         const float gsum = wave_reduce_multi<2 * kGuRows>(acc, lane);
         const float usum = shfl_xor(gsum, WAVE / 2);
-        const int r = (lane >> 3) & (kGuRows - 1);
-        if (lane < WAVE / 2 && (lane & 7) == 0) {
+        const int r = lane / kLanesPerVal;
+        if (lane < WAVE / 2 && lane % kLanesPerVal == 0) {
             int hi = hidx[0];
 #pragma unroll
             for (int q = 1; q < kGuRows; ++q) hi = r == q ? hidx[q] : hi;

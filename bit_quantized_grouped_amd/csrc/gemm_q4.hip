@@ -46,10 +46,10 @@
 #define MOE_GU_DEPTH 4
 #endif
 #ifndef MOE_DN_WAVES
-#define MOE_DN_WAVES 4
+#define MOE_DN_WAVES 8
 #endif
 #ifndef MOE_DN_NSUB
-#define MOE_DN_NSUB 2
+#define MOE_DN_NSUB 1
 #endif
 #ifndef MOE_DN_KC
 #define MOE_DN_KC 128

@@ -6,7 +6,7 @@
 //   gate[t] = sigmoid(sum_h x[t, h] * w_g[h])
 // computed as one more output row of the same product.
 //
-// A workgroup owns 16 tokens x 16 output rows; its 4 waves split the K range
+// A workgroup owns 16 tokens x 16 output rows; its 8 waves split the K range
 // (32-wide steps, round robin) and sum their v_mfma_f32_16x16x32_bf16
 // accumulators through LDS.  Both operands are read straight from memory in
 // the MFMA layout: lane l supplies x[t0 + l%16][k0 + 8(l/16) .. +8] and
@@ -17,7 +17,7 @@
 
 namespace moeq4 {
 
-constexpr int kRtWaves = 4;
+constexpr int kRtWaves = 8;
 constexpr int kRtUnroll = 8;   // K steps whose loads a wave issues together
 
 __global__ __launch_bounds__(kRtWaves * WAVE) void router_kernel(
