@@ -3,6 +3,10 @@
 One step = one full layer call (moe_route -> moe_grouped_gemm_q4 ->
 moe_combine) over the 512-token prefill workload (H 2048, I 512, 256 experts
 top-8 + 1 shared expert of I 512, 4-bit g64 weights), inputs resident in HBM.
+The weights' code words are put in the tile-packed order once at load time
+(moe_q4_prepack, outside every timed region); --layout rows times the
+row-major order instead, and the other layout's 512-token figure is always
+reported next to it.
 Prints ONE JSON line.  The 2048-token prefill, batch-1 decode over 1000
 tokens and the skewed 8192-token prefill in chunks of 2048 are timed too and
 reported under "extra".
@@ -65,6 +69,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--block-rows", type=int, default=32)
+    ap.add_argument("--layout", choices=("tiles", "rows"), default="tiles",
+                    help="code-word layout of the timed layer: tile-packed (load-time "
+                         "moe_q4_prepack) or row-major; the other one's prefill512 is reported too")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run")
@@ -195,14 +202,22 @@ def main():
     cfg = CONFIGS["prefill512"]
     log("generating weights")
     w = make_weights(cfg, seed=0)
-    layer = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
-    log("weights resident")
+    layer_rows = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev,
+                             block_rows=args.block_rows)
+    # load time, outside every timed region: the same weights with tile-packed code words
+    layer_tiles = bq.MoeLayer.from_device(
+        [None if m is None else m.prepacked() for m in layer_rows.weight_mats()],
+        cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
+    torch.cuda.synchronize()
+    layer, other = ((layer_tiles, layer_rows) if args.layout == "tiles"
+                    else (layer_rows, layer_tiles))
+    log(f"weights resident (timed layout: {args.layout})")
     br = layer.block_rows
     mats0 = layer.weight_mats()
     layers = [layer] + [
         bq.MoeLayer.from_device(
             [None if m is None else bq.DeviceQMat(m.codes ^ (0x01010101 * i), m.scales.clone(),
-                                                  m.biases.clone()) for m in mats0],
+                                                  m.biases.clone(), m.layout) for m in mats0],
             cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
         for i in range(1, 4)]
     log("4 layer copies resident (cold runs)")
@@ -273,7 +288,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill512", "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "I_shared": cfg.I_sh, "block_rows": br,
-                   "weights": "4-bit codes, bf16 scale+bias per 64 along K"},
+                   "weights": "4-bit codes, bf16 scale+bias per 64 along K",
+                   "code_layout": "tile-packed at load time (moe_q4_prepack)" if args.layout == "tiles"
+                                  else "row-major"},
         "roofline": {"bound": "hbm", "kernel": "grouped_q4_kernel gate/up+SwiGLU (moe_expert_gateup_q4)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": read_traffic(),
@@ -291,12 +308,20 @@ def main():
         f"gateup {t_gu*1e6:.1f} ({achieved/1e9:.0f} GB/s) down {t_dn*1e6:.1f} "
         f"combine {t_comb*1e6:.1f} us; cold {ms_cold*1e3:.1f} us/call")
 
+    # ---------------- the other code-word layout, same weights ----------------
+    other_name = "rows" if args.layout == "tiles" else "tiles"
+    ms_ot = timed(lambda: other.forward(x, lg), args.steps, args.warmup, torch)
+    result["layer"][f"{other_name}_layout_us_per_call"] = ms_ot * 1e3
+    result["layer"][f"{other_name}_layout_tokens_per_s"] = T / (ms_ot * 1e-3)
+    log(f"prefill512 with {other_name} code layout: {ms_ot*1e3:.1f} us/call ({T/(ms_ot*1e-3):,.0f} tok/s)")
+
     # ---------------- the pages' two ablations (512 tokens) ----------------
     extra = {}
     if not args.no_extra and (not only_set(args) or "ablations" in only_set(args)):
-        ms_unf = timed(lambda: layer.forward_unfused(x, lg), max(20, args.steps // 4), 5, torch)
+        # the expansion reads row-major code words
+        ms_unf = timed(lambda: layer_rows.forward_unfused(x, lg), max(20, args.steps // 4), 5, torch)
         y_fused = layer.forward(x, lg)["y"].clone()
-        y_unf = layer.forward_unfused(x, lg)["y"]
+        y_unf = layer_rows.forward_unfused(x, lg)["y"]
         torch.cuda.synchronize()
         err = float((y_unf.float() - y_fused.float()).abs().max() / y_fused.float().abs().max())
         extra["ablation_unfused"] = {

@@ -31,8 +31,13 @@ class MoeError(RuntimeError):
         super().__init__(f"{where}: status {status} ({status_str(status)})")
 
 
+LAYOUT_ROWS = 0      # row-major code words
+LAYOUT_TILES = 1     # tile-packed code words (moe_q4_prepack)
+
+
 class MoeQ4Mat(ctypes.Structure):
-    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("layout", ctypes.c_int32)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -61,6 +66,7 @@ _SIGNATURES = {
                            + [ctypes.POINTER(MoeQ4Mat)] * 2 + [_P, _P, _P, _S, _P]),
     "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
     "moe_dequant_q4_bf16": (_I, [ctypes.POINTER(MoeQ4Mat), _I, _I, _I, _P, _P, _P]),
+    "moe_q4_prepack": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_combine_gated": (_I, [_P, _P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
     "moe_router": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P]),
     "moe_expert_gateup_bf16": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
@@ -122,9 +128,20 @@ def _stream(stream, device):
 class DeviceQMat:
     """One 4-bit matrix set [n_exp, N, K] resident on the device."""
 
-    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor):
-        self.codes, self.scales, self.biases = codes, scales, biases
-        self.struct = MoeQ4Mat(codes.data_ptr(), scales.data_ptr(), biases.data_ptr())
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                 layout: int = LAYOUT_ROWS):
+        self.codes, self.scales, self.biases, self.layout = codes, scales, biases, layout
+        self.struct = MoeQ4Mat(codes.data_ptr(), scales.data_ptr(), biases.data_ptr(), layout)
+
+    def prepacked(self, stream=None) -> "DeviceQMat":
+        """The same matrices with the code words in the tile-packed order (scales and biases
+        are shared with this object)."""
+        assert self.layout == LAYOUT_ROWS
+        n_exp, N, G = self.scales.shape
+        dst = torch.empty_like(self.codes)
+        _check(lib().moe_q4_prepack(_ptr(self.codes), n_exp, N, G * 64, _ptr(dst),
+                                    _stream(stream, dst.device)), "moe_q4_prepack")
+        return DeviceQMat(dst, self.scales, self.biases, LAYOUT_TILES)
 
     @classmethod
     def from_host(cls, m, device) -> "DeviceQMat":
@@ -337,7 +354,7 @@ class MoeLayer:
     """Device-resident weights of one layer plus per-call buffers for T tokens."""
 
     def __init__(self, weights, H: int, I: int, I_sh: int, E: int, k: int, device,
-                 block_rows: int = 32):
+                 block_rows: int = 32, prepack: bool = False):
         self.H, self.I, self.I_sh, self.E, self.k = H, I, I_sh, E, k
         self.block_rows = block_rows
         self.device = torch.device(device)
@@ -345,6 +362,12 @@ class MoeLayer:
         self.gate, self.up, self.down = up(weights.gate), up(weights.up), up(weights.down)
         self.sh_gate, self.sh_up, self.sh_down = (up(weights.sh_gate), up(weights.sh_up),
                                                   up(weights.sh_down))
+        if prepack:   # load time: code words into the tile-packed order, row-major copies freed
+            for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+                m = getattr(self, name)
+                if m is not None:
+                    setattr(self, name, m.prepacked())
+            torch.cuda.synchronize(self.device)
         self._bufs = {}
 
     @classmethod

@@ -1,6 +1,7 @@
 // C ABI of the 4-bit grouped MoE layer: host-side validation, workspace
 // layout and kernel dispatch.  Every entry point validates first and
 // enqueues nothing on failure; none allocates, frees or synchronises.
+#include <initializer_list>
 #include <new>
 
 #include "../../include/moe_q4.h"
@@ -10,7 +11,7 @@ using namespace moeq4;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kMaxE = 1000;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -38,6 +39,18 @@ int check_mat(const moe_q4_mat* m) {
     if (!m || !m->codes || !m->scales || !m->biases) return MOE_ERR_NULL;
     if (!aligned(m->codes, 16) || !aligned(m->scales, 2) || !aligned(m->biases, 2))
         return MOE_ERR_ALIGN;
+    if (m->layout != MOE_Q4_LAYOUT_ROWS && m->layout != MOE_Q4_LAYOUT_TILES) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+// Every non-NULL matrix of one call shares the first one's layout.
+static int check_same_layout(std::initializer_list<const moe_q4_mat*> mats) {
+    int layout = -1;
+    for (const moe_q4_mat* m : mats) {
+        if (!m) continue;
+        if (layout < 0) layout = m->layout;
+        else if (m->layout != layout) return MOE_ERR_SHAPE;
+    }
     return MOE_OK;
 }
 
@@ -59,8 +72,8 @@ RoutingDev to_dev(const moe_routing* r) {
 }
 
 QMatDev to_dev(const moe_q4_mat* m) {
-    if (!m) return QMatDev{nullptr, nullptr, nullptr};
-    return QMatDev{m->codes, m->scales, m->biases};
+    if (!m) return QMatDev{nullptr, nullptr, nullptr, 0};
+    return QMatDev{m->codes, m->scales, m->biases, m->layout};
 }
 
 // Layout of moe_layer_chunked's workspace for chunks of C tokens.
@@ -118,6 +131,7 @@ int gemm_args_ok(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
     } else if (sh_gate || sh_up || sh_down || shared_out) {
         return MOE_ERR_SHAPE;   // shared matrices given but I_sh == 0
     }
+    if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
     if (!aligned(x, 16) || !aligned(expert_out, 16)) return MOE_ERR_ALIGN;
     return MOE_OK;
 }
@@ -250,6 +264,7 @@ int moe_expert_gateup_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E
         } else if (sh_gate || sh_up) {
             return MOE_ERR_SHAPE;
         }
+        if ((st = check_same_layout({gate, up, sh_gate, sh_up}))) return st;
         if (!aligned(x, 16)) return MOE_ERR_ALIGN;
         if ((st = check_ws(ws, ws_bytes, moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))))
             return st;
@@ -271,6 +286,7 @@ int moe_expert_down_q4(int T, int H, int I, int I_sh, int E, int k, int block_ro
         if (!expert_out) return MOE_ERR_NULL;
         if ((st = check_routing(r))) return st;
         if ((st = check_mat(down))) return st;
+        if ((st = check_same_layout({down, sh_down}))) return st;
         if (I_sh) {
             if (!shared_out) return MOE_ERR_NULL;
             if ((st = check_mat(sh_down))) return st;
@@ -290,6 +306,22 @@ int moe_expert_down_q4(int T, int H, int I, int I_sh, int E, int k, int block_ro
     }
 }
 
+int moe_q4_prepack(const uint32_t* src_codes, int n_exp, int N, int K, uint32_t* dst_codes,
+                   hipStream_t stream) {
+    try {
+        if (n_exp < 1 || N < 64 || N % 64 || K < 64 || K % 64) return MOE_ERR_SHAPE;
+        if ((size_t)n_exp * N * (K / 8) >= ((size_t)1 << 31)) return MOE_ERR_SHAPE;
+        if (!src_codes || !dst_codes) return MOE_ERR_NULL;
+        if (src_codes == dst_codes) return MOE_ERR_SHAPE;
+        if (!aligned(src_codes, 16) || !aligned(dst_codes, 16)) return MOE_ERR_ALIGN;
+        return launch_prepack(src_codes, n_exp, N, K, dst_codes, stream) == hipSuccess
+                   ? MOE_OK
+                   : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
 int moe_dequant_q4_bf16(const moe_q4_mat* m, int n_exp, int N, int K, const int32_t* counts,
                         uint16_t* out, hipStream_t stream) {
     try {
@@ -297,6 +329,7 @@ int moe_dequant_q4_bf16(const moe_q4_mat* m, int n_exp, int N, int K, const int3
         if ((size_t)n_exp * N * (K / 8) >= ((size_t)1 << 31)) return MOE_ERR_SHAPE;
         int st = check_mat(m);
         if (st) return st;
+        if (m->layout != MOE_Q4_LAYOUT_ROWS) return MOE_ERR_UNIMPLEMENTED;   // expands row-major codes
         if (!out) return MOE_ERR_NULL;
         if (!aligned(out, 16)) return MOE_ERR_ALIGN;
         return launch_dequant_bf16(to_dev(m), n_exp, N, K, counts, out, stream) == hipSuccess
@@ -442,6 +475,7 @@ int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh
         } else if (sh_gate || sh_up || sh_down) {
             return MOE_ERR_SHAPE;
         }
+        if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
         if (r && (st = check_routing(r))) return st;
         if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4)) return MOE_ERR_ALIGN;
         size_t off_idx = 0, off_w = 0;
@@ -516,6 +550,7 @@ int moe_layer_chunked(const uint16_t* x, const float* logits, int T, int H, int 
         } else if (sh_gate || sh_up || sh_down) {
             return MOE_ERR_SHAPE;
         }
+        if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
         if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, 256))
             return MOE_ERR_ALIGN;
         const LayerWs L = layer_ws_layout(C, H, I, I_sh, E, k, block_rows);

@@ -163,10 +163,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
     const float unit_inv = 1.0f / fp8_unit();
     const int stride = gridDim.x * kDecWaves * kGuRows;
     for (int t0 = (blockIdx.x * kDecWaves + wave) * kGuRows; t0 < n_tasks; t0 += stride) {
-        const uint32_t* gc[kGuRows];
+        const uint32_t* gc[kGuRows];   // expert's code matrix (row n_r is addressed per layout)
         const uint32_t* uc[kGuRows];
         const uint16_t *gs[kGuRows], *gb[kGuRows], *us[kGuRows], *ub[kGuRows];
-        int hidx[kGuRows];
+        int hidx[kGuRows], nrow[kGuRows];
 #pragma unroll
         for (int r = 0; r < kGuRows; ++r) {
             const int t = t0 + r < n_tasks ? t0 + r : n_tasks - 1;   // tail: re-read a valid row
@@ -176,8 +176,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
             const size_t row = sh ? (size_t)n : (size_t)__builtin_amdgcn_readfirstlane(s_idx[j]) * I + n;
             const QMatDev& g = sh ? p.sh_gate : p.gate;
             const QMatDev& u = sh ? p.sh_up : p.up;
-            gc[r] = g.codes + row * (H / 8);
-            uc[r] = u.codes + row * (H / 8);
+            const size_t ebase = (row - n) * (H / 8);   // first word of the expert's matrix
+            gc[r] = g.codes + ebase;
+            uc[r] = u.codes + ebase;
+            nrow[r] = n;
             gs[r] = g.scales + row * (H / 64);
             gb[r] = g.biases + row * (H / 64);
             us[r] = u.scales + row * (H / 64);
@@ -196,8 +198,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
             const int grp = kb / 64;
 #pragma unroll
             for (int r = 0; r < kGuRows; ++r) {
-                gw[r] = *(const u32x4_t*)(gc[r] + kb / 8);
-                uw[r] = *(const u32x4_t*)(uc[r] + kb / 8);
+                const uint32_t wo = code_word(p.gate.layout, nrow[r], kb / 8, H);
+                gw[r] = *(const u32x4_t*)(gc[r] + wo);
+                uw[r] = *(const u32x4_t*)(uc[r] + wo);
                 sg[r] = bf16_to_f32(gs[r][grp]);
                 bg[r] = bf16_to_f32(gb[r][grp]);
                 su[r] = bf16_to_f32(us[r][grp]);
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) 
             N[i] = !on ? 0 : sh ? I_sh : I;
             const int Nr = N[i] ? N[i] : 64;
             const size_t row = (size_t)e * H + c;
-            dc[i] = d.codes + row * (Nr / 8);
+            dc[i] = d.codes + (size_t)e * H * (Nr / 8);   // expert's code matrix; row c per layout
             ds[i] = d.scales + row * (Nr / 64);
             db[i] = d.biases + row * (Nr / 64);
             hp[i] = p.h + (size_t)(on ? j : 0) * ldh;
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) 
 #pragma unroll
             for (int i = 0; i < kDnExp; ++i) {
                 if (kb < N[i]) {
-                    cw[i] = *(const u32x4_t*)(dc[i] + kb / 8);
+                    cw[i] = *(const u32x4_t*)(dc[i] + code_word(p.down.layout, c, kb / 8, N[i]));
                     s[i] = bf16_to_f32(ds[i][kb / 64]);
                     b[i] = bf16_to_f32(db[i][kb / 64]);
 #pragma unroll

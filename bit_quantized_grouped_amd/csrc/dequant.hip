@@ -1,5 +1,7 @@
-// Expansion of 4-bit groupwise-affine weights into a bf16 matrix in memory:
-// the unfused layout that the pages measure the fused grouped GEMM against
+// Weight-format utilities: the load-time repack of code words into the
+// tile-packed order, and the expansion of 4-bit groupwise-affine weights
+// into a bf16 matrix in memory, the unfused layout that the pages measure
+// the fused grouped GEMM against
 // ([P2] aikraft.ru, "Technical optimizations: Prefill and Decode"; [P3]
 // droneth.or.th, ablation paragraph: building the dequantization into the
 // grouped GEMM instead was worth +77.4 % at 512 tokens).
@@ -27,6 +29,30 @@ __global__ __launch_bounds__(kDqThreads) void dequant_q4_bf16_kernel(
     const float s = bf16_to_f32(m.scales[sidx]) * (1.0f / fp8_unit());
     const float b = bf16_to_f32(m.biases[sidx]);
     *(bf16x8_t*)(out + (size_t)w * 8) = dequant_word(m.codes[w], s, b);
+}
+
+// Code words into the tile-packed order (moe_q4_prepack, load time): each
+// thread moves 4 consecutive words (16 bytes) of a row-major row to their
+// place in the packed order, where they are again consecutive.
+__global__ __launch_bounds__(kDqThreads) void prepack_kernel(const uint32_t* __restrict__ src,
+                                                          uint32_t N, uint32_t K, uint32_t quads,
+                                                          uint32_t* __restrict__ dst) {
+    const uint32_t q = blockIdx.x * kDqThreads + threadIdx.x;
+    if (q >= quads) return;
+    const uint32_t w = q * 4;
+    const uint32_t words_per_row = K / 8;
+    const uint32_t row = w / words_per_row, c = w % words_per_row;   // row = e * N + n
+    const uint32_t e = row / N, n = row % N;
+    const size_t to = (size_t)e * N * words_per_row + code_word(1, n, c, K);
+    *(u32x4_t*)(dst + to) = *(const u32x4_t*)(src + w);
+}
+
+hipError_t launch_prepack(const uint32_t* src, int n_exp, int N, int K, uint32_t* dst,
+                          hipStream_t stream) {
+    const uint32_t quads = (uint32_t)((size_t)n_exp * N * (K / 8) / 4);
+    prepack_kernel<<<(quads + kDqThreads - 1) / kDqThreads, kDqThreads, 0, stream>>>(
+        src, (uint32_t)N, (uint32_t)K, quads, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_dequant_bf16(const QMatDev& m, int n_exp, int N, int K, const int32_t* counts,

@@ -120,7 +120,10 @@ template <int NMAT, int NSUB, int KC>
 struct Streams {
     rsrc_t codes[NMAT];
     int voff_c;                       // per-lane byte offset (row, lane group)
-    int sub_c;                        // byte stride of 16 rows in codes
+    int sub_c;                        // byte offset of subtile s is s * sub_c (row-major, bf16)
+    int sub_off[NSUB];                // byte offset of subtile s (tile-packed codes)
+    int chunk_c;                      // byte step per K-chunk in codes
+    bool tiles;                       // codes are tile-packed
 };
 
 // Chunks past the last one (pipeline run-out) are requested with kVoffOob
@@ -148,7 +151,7 @@ __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                      S.codes[m], S.voff_c + voff_oob + 16 * j, so_b, 0));
                 continue;
             }
-            const int so_c = s * S.sub_c + c * (KC / 2);
+            const int so_c = (S.tiles ? S.sub_off[s] : s * S.sub_c) + c * S.chunk_c;
             if constexpr (W >= 4) {
 #pragma unroll
                 for (int j = 0; j < W / 4; ++j)
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     __shared__ int s_row[MT];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int nl = lane & 15, g = lane >> 4;
 
     // ---- work item ----
@@ -316,12 +319,27 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         }
     }
     const int row_lane = wave * NSUB * 16 + nl;     // lane's row within the tile
+    S.tiles = false;
     if constexpr (BF) {
         S.voff_c = (n_base + row_lane) * (K * 2) + g * W * 16;
         S.sub_c = 16 * (K * 2);
     } else {
+        S.tiles = (is_sh ? p.sB[0] : p.rB[0]).layout != 0;
         S.voff_c = (n_base + row_lane) * (K / 2) + g * W * 4;
         S.sub_c = 16 * (K / 2);
+        S.chunk_c = KC / 2;
+        if (S.tiles) {
+            // 64-row tiles x 64-K blocks of 2 KB (16-row groups of 512 B, rows of 32 B);
+            // this wave's first 16-row group is rg0 of the workgroup's tile-aligned rows
+            const int rg0 = wave * NSUB;
+            const int kb = g * W * 8;                    // lane's first weight in the chunk
+            auto group_off = [&](int rg) { return (rg / 4) * (K / 64) * 2048 + (rg % 4) * 512; };
+            S.voff_c = (n_base / 64) * (K / 64) * 2048 + group_off(rg0) + (kb / 64) * 2048 +
+                       nl * 32 + (kb % 64) / 2;
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) S.sub_off[s] = group_off(rg0 + s) - group_off(rg0);
+            S.chunk_c = (KC / 64) * 2048;
+        }
     }
     const int lane_grp = (g * (KC / 4)) / 64;
     const uint16_t* sSc_lane = sSc + row_lane * GS + lane_grp;

@@ -56,6 +56,16 @@ __device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, float s_scaled, flo
     return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// Offset, in words, of code word c (weights 8c .. 8c+7) of row n of one
+// expert's [N, K] code matrix.  Layout 0 is row-major; layout 1 stores, per
+// tile of 64 rows and per 64 K, the tile's rows together (16-row groups of
+// 16 rows x 8 words), so a tile's K-chunk is one contiguous block.  Four
+// consecutive words c .. c+3 with c % 4 == 0 are contiguous in both.
+__device__ __forceinline__ uint32_t code_word(int layout, uint32_t n, uint32_t c, uint32_t K) {
+    if (layout == 0) return n * (K / 8) + c;
+    return ((n / 64) * (K / 64) + c / 8) * 512 + ((n % 64) / 16) * 128 + (n % 16) * 8 + c % 8;
+}
+
 // D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate.
 // Lane l supplies A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16];
 // it holds D[4*(l/16) + i][l%16], i = 0..3.

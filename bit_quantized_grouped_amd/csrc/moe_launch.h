@@ -14,6 +14,7 @@ struct QMatDev {
     const uint32_t* codes;
     const uint16_t* scales;
     const uint16_t* biases;
+    int layout;               // 0 = row-major code words, 1 = tile-packed (moe_q4_prepack)
 };
 
 struct RoutingDev {
@@ -53,6 +54,8 @@ hipError_t launch_down_bf16(const GemmProblem& p, const uint16_t* down, const ui
                             const void* ws, hipStream_t stream);
 
 // dequant.hip
+hipError_t launch_prepack(const uint32_t* src, int n_exp, int N, int K, uint32_t* dst,
+                          hipStream_t stream);
 hipError_t launch_dequant_bf16(const QMatDev& m, int n_exp, int N, int K, const int32_t* counts,
                                uint16_t* out, hipStream_t stream);
 

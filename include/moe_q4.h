@@ -58,18 +58,27 @@ extern "C" {
 #define MOE_ERR_HIP           -5  /* a kernel launch failed (hipGetLastError) */
 #define MOE_ERR_UNIMPLEMENTED -6  /* combination not built into this library */
 
-/* One set of 4-bit matrices [n_exp, N, K] (row-major, K innermost):
- *   codes  uint32 [n_exp, N, K/8]: code of weight (n, 8c+i) in bits 4i..4i+3
- *          of word c (lowest k in the low nibble); 16-byte aligned;
+/* One set of 4-bit matrices [n_exp, N, K] (K innermost):
+ *   codes  uint32, n_exp*N*K/8 words, 16-byte aligned: code of weight
+ *          (n, 8c+i) in bits 4i..4i+3 of its word (lowest k in the low
+ *          nibble); the words are ordered by `layout`:
+ *            MOE_Q4_LAYOUT_ROWS   word (n, c) at n*(K/8) + c (row-major);
+ *            MOE_Q4_LAYOUT_TILES  the tile-packed order moe_q4_prepack
+ *                                 writes (see there);
  *   scales bf16   [n_exp, N, K/64]: scale of weights (n, 64g .. 64g+63);
- *   biases bf16   [n_exp, N, K/64].
+ *   biases bf16   [n_exp, N, K/64] (row-major in both layouts).
  * Weight value: w = bf16_rne(fp32(q * scale + bias)) ([P1] "Prefill
  * optimizations"; [P3] "A big model ...").  Gate and up are [E, I, H],
- * down is [E, H, I]; the shared expert's are [1, I_sh, H] and [1, H, I_sh]. */
+ * down is [E, H, I]; the shared expert's are [1, I_sh, H] and [1, H, I_sh].
+ * A zero-initialised layout is MOE_Q4_LAYOUT_ROWS.  The matrices passed to
+ * one call must share one layout. */
+#define MOE_Q4_LAYOUT_ROWS  0
+#define MOE_Q4_LAYOUT_TILES 1
 typedef struct {
     const uint32_t* codes;
     const uint16_t* scales;
     const uint16_t* biases;
+    int32_t layout;
 } moe_q4_mat;
 
 /* Routing results of one layer call (all device arrays, caller-allocated).
@@ -223,6 +232,20 @@ int moe_combine_gated(const uint16_t* expert_out, const uint16_t* shared_out,
  * 1 <= E <= 1000.  Enqueues one kernel. */
 int moe_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
                const uint16_t* w_gate, float* logits, float* gate, hipStream_t stream);
+
+/* Repack the code words of a row-major matrix set [n_exp, N, K] into the
+ * tile-packed order (load time; scales and biases keep their layout).  For
+ * each expert, each tile of 64 rows and each run of 64 K, the 64 rows' 32
+ * bytes are stored together: word (n, c) goes to
+ *   e*N*K/8 + ((n'/64)*(K/64) + c/8)*512 + ((n'%64)/16)*128 + (n'%16)*8 + c%8
+ * where n = e*N + n'.  A grouped-GEMM chunk of one tile is then one
+ * contiguous 2 KB (64 K) or 4 KB (128 K) block instead of 64 row pieces,
+ * which the memory system streams at a higher rate.  src and dst are
+ * distinct device buffers of n_exp*N*K/8 words, 16-byte aligned; N and K
+ * multiples of 64, n_exp*N*K/8 < 2^31.  Enqueues one kernel; the returned
+ * matrix for later calls is {dst, src scales, src biases, MOE_Q4_LAYOUT_TILES}. */
+int moe_q4_prepack(const uint32_t* src_codes, int n_exp, int N, int K, uint32_t* dst_codes,
+                   hipStream_t stream);
 
 /* Device workspace bytes moe_decode_q4 needs (0 on bad shapes). */
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k);

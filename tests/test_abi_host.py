@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert bq.abi_version() == 1
+    assert bq.abi_version() == 2
     for st, txt in [(0, "ok"), (-1, "null pointer"), (-2, "bad shape"), (-3, "misaligned pointer"),
                     (-4, "workspace too small"), (-5, "HIP launch error"), (-6, "unimplemented"),
                     (-99, "unknown status")]:
@@ -216,3 +216,25 @@ def test_router_and_gated_combine_reject_bad_arguments():
     assert cg(g=None) == bq.MOE_ERR_NULL
     assert cg(g=P(0x10002)) == bq.MOE_ERR_ALIGN
     assert cg(y=MISALIGNED) == bq.MOE_ERR_ALIGN
+
+
+def test_layout_validation():
+    L = bq.lib()
+    r = _routing()
+    ws = bq.gemm_workspace_bytes(64, 256, 128, 128, 16, 2, 32)
+    rows, tiles, bad = _mat(), _mat(), _mat()
+    tiles.layout, bad.layout = bq.LAYOUT_TILES, 7
+    gu = lambda mats: L.moe_expert_gateup_q4(  # noqa: E731
+        FAKE, 64, 256, 128, 128, 16, 2, 32, ctypes.byref(r), *[ctypes.byref(q) for q in mats],
+        FAKE, ws, None)
+    assert gu([bad, bad, bad, bad]) == bq.MOE_ERR_SHAPE                 # unknown layout
+    assert gu([rows, tiles, rows, rows]) == bq.MOE_ERR_SHAPE            # mixed layouts
+    assert L.moe_dequant_q4_bf16(ctypes.byref(tiles), 4, 64, 128, None, FAKE, None) \
+        == bq.MOE_ERR_UNIMPLEMENTED                                     # expands row-major only
+    pp = lambda src=FAKE, N=64, K=128, dst=P(0x20000): L.moe_q4_prepack(  # noqa: E731
+        src, 2, N, K, dst, None)
+    assert pp(src=None) == bq.MOE_ERR_NULL
+    assert pp(N=96) == bq.MOE_ERR_SHAPE
+    assert pp(K=100) == bq.MOE_ERR_SHAPE
+    assert pp(dst=FAKE) == bq.MOE_ERR_SHAPE                             # in place
+    assert pp(dst=MISALIGNED) == bq.MOE_ERR_ALIGN

@@ -1,0 +1,94 @@
+"""Tile-packed code words (moe_q4_prepack): the repack is exactly the
+permutation the header documents, and every output of the layer, of decode
+and of the split phases is bit-identical to the row-major layout's (only the
+addresses of the code words change, not the arithmetic or its order)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_grouped_amd as bq
+from gpu_cases import DEV, announce, layer_to_host, require_gpu, run_layer
+from workload import CONFIGS, make_activations, make_weights, small_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _packed_reference(codes, N, K):
+    """The header's formula, word by word: (e, n, c) -> e*N*K/8 + ((n/64)*(K/64) + c/8)*512
+    + ((n%64)/16)*128 + (n%16)*8 + c%8."""
+    n_exp = codes.shape[0]
+    out = np.empty(codes.size, codes.dtype)
+    e, n, c = np.meshgrid(np.arange(n_exp), np.arange(N), np.arange(K // 8), indexing="ij")
+    to = (e * N * (K // 8) + ((n // 64) * (K // 64) + c // 8) * 512 + ((n % 64) // 16) * 128
+          + (n % 16) * 8 + c % 8)
+    out[to.reshape(-1)] = codes.reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("n_exp,N,K", [(3, 128, 192), (2, 64, 64), (1, 512, 2048)])
+def test_prepack_is_the_documented_permutation(n_exp, N, K):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 2 ** 32, (n_exp, N, K // 8), dtype=np.uint32)
+    src = torch.from_numpy(codes.view(np.int32)).to(DEV)
+    dst = torch.zeros_like(src)
+    announce(f"prepack permutation {n_exp}x{N}x{K}")
+    assert bq.lib().moe_q4_prepack(src.data_ptr(), n_exp, N, K, dst.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint32).reshape(-1)
+    want = _packed_reference(codes, N, K)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.sort(got), np.sort(codes.reshape(-1)))
+
+
+SHAPES = [
+    # T,   H,    I,   E,  k, I_sh, block_rows
+    (64, 256, 128, 16, 2, 128, 32),
+    (200, 512, 256, 32, 4, 256, 32),
+    (37, 256, 128, 8, 3, 0, 16),
+    (130, 384, 192, 12, 2, 320, 64),      # K = 192 and 320: the 64-K chunk path
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,I_sh,block_rows", SHAPES)
+def test_layer_outputs_identical_in_both_layouts(T, H, I, E, k, I_sh, block_rows):
+    cfg = small_config(T, H, I, E, k, I_sh, seed=T + 1)
+    w = make_weights(cfg, seed=T + H + 1, cache=False)
+    x_bits, logits = make_activations(cfg)
+    rows = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=block_rows)
+    tiles = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=block_rows, prepack=True)
+    assert tiles.gate.layout == bq.LAYOUT_TILES
+    announce(f"layouts T={T} H={H} I={I} E={E} k={k} I_sh={I_sh} br={block_rows}")
+    a = run_layer(rows, x_bits, logits)
+    b = run_layer(tiles, x_bits, logits)
+    for key in ("y", "expert_out") + (("shared_out",) if I_sh else ()):
+        assert np.array_equal(a[key], b[key]), key
+    # decode: token by token through the two-launch path
+    for t in (0, T - 1):
+        ys = []
+        for L in (rows, tiles):
+            x = bq.bf16_from_bits(x_bits[t:t + 1], DEV)
+            lg = torch.from_numpy(np.ascontiguousarray(logits[t:t + 1])).to(DEV)
+            y = torch.empty((1, H), dtype=torch.bfloat16, device=DEV)
+            L.decode(x, lg, y)
+            torch.cuda.synchronize()
+            ys.append(bq.bf16_to_bits(y))
+        assert np.array_equal(ys[0], ys[1]), f"decode token {t}"
+
+
+def test_prefill512_identical_in_both_layouts():
+    cfg = CONFIGS["prefill512"]
+    w = make_weights(cfg, seed=0)
+    rows = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
+    tiles = bq.MoeLayer.from_device([None if m is None else m.prepacked() for m in rows.weight_mats()],
+                                    cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
+    x_bits, logits = make_activations(cfg)
+    announce("layouts prefill512")
+    a = run_layer(rows, x_bits, logits)
+    b = run_layer(tiles, x_bits, logits)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["expert_out"], b["expert_out"])
