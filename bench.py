@@ -67,7 +67,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first; the GPU needs about 30 ms of work to reach its steady clock")
     ap.add_argument("--block-rows", type=int, default=32)
     ap.add_argument("--layout", choices=("tiles", "rows"), default="tiles",
                     help="code-word layout of the timed layer: tile-packed (load-time "
