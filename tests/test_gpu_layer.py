@@ -269,6 +269,9 @@ def test_fused_decode_sequential_equals_single(big_layer):
     (256, 128, 16, 2, 128),      # the tiny layer's shape
     (512, 256, 100, 7, 0),       # no shared expert, E not a multiple of 64
     (384, 192, 8, 1, 320),       # I_sh != I, k = 1
+    (256, 1024, 64, 16, 768),    # k + 1 > 12 experts per down workgroup, K of down > 512
+    (4096, 64, 8, 2, 64),        # H > 2048: several K passes per gate/up row
+    (128, 128, 256, 64, 128),    # the largest k
 ])
 def test_fused_decode_small_shapes(H, I, E, k, I_sh):
     cfg = small_config(6, H, I, E, k, I_sh, seed=E + k)
