@@ -64,6 +64,8 @@ _SIGNATURES = {
                              + [ctypes.POINTER(MoeQ4Mat)] * 4 + [_P, _S, _P]),
     "moe_expert_down_q4": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
                            + [ctypes.POINTER(MoeQ4Mat)] * 2 + [_P, _P, _P, _S, _P]),
+    "moe_layer_q4": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(MoeQ4Mat)] * 6
+                     + [ctypes.POINTER(MoeRouting), _P, _S, _P, _P, _P, _S, _P, _P]),
     "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
     "moe_dequant_q4_bf16": (_I, [ctypes.POINTER(MoeQ4Mat), _I, _I, _I, _P, _P, _P]),
     "moe_q4_prepack": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -246,6 +248,20 @@ def moe_expert_down_q4(T: int, H: int, I: int, I_sh: int, E: int, k: int, block_
         _stream(stream, expert_out.device)), "moe_expert_down_q4")
 
 
+def moe_layer_q4(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, E: int, k: int,
+                 block_rows: int, routing: DeviceRouting, route_ws: torch.Tensor, gate, up, down,
+                 sh_gate, sh_up, sh_down, expert_out: torch.Tensor, shared_out,
+                 gemm_ws: torch.Tensor, y: torch.Tensor, stream=None):
+    T, H = x.shape
+    _check(lib().moe_layer_q4(
+        _ptr(x), _ptr(logits), T, H, I, I_sh, E, k, block_rows,
+        _mat(gate), _mat(up), _mat(down), _mat(sh_gate), _mat(sh_up), _mat(sh_down),
+        ctypes.byref(routing.struct), _ptr(route_ws), route_ws.numel() * route_ws.element_size(),
+        _ptr(expert_out), _ptr(shared_out), _ptr(gemm_ws),
+        gemm_ws.numel() * gemm_ws.element_size(), _ptr(y), _stream(stream, x.device)),
+        "moe_layer_q4")
+
+
 def moe_combine(expert_out: torch.Tensor, shared_out, routing: DeviceRouting, k: int,
                 y: torch.Tensor, stream=None):
     T, H = y.shape
@@ -404,7 +420,19 @@ class MoeLayer:
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, out: torch.Tensor | None = None,
                 stream=None) -> dict:
-        """route -> grouped GEMM -> combine on one stream; returns the buffers used."""
+        """One moe_layer_q4 call (route -> grouped GEMM -> combine on one stream);
+        returns the buffers used."""
+        T = x.shape[0]
+        b = self.buffers(T)
+        y = b["y"] if out is None else out
+        moe_layer_q4(x, logits, self.I, self.I_sh, self.E, self.k, self.block_rows, b["routing"],
+                     b["route_ws"], *self.weight_mats(), b["expert_out"], b["shared_out"],
+                     b["gemm_ws"], y, stream)
+        return dict(b, y=y)
+
+    def forward_three_calls(self, x: torch.Tensor, logits: torch.Tensor,
+                            out: torch.Tensor | None = None, stream=None) -> dict:
+        """moe_route, moe_grouped_gemm_q4 and moe_combine in order on one stream."""
         T = x.shape[0]
         b = self.buffers(T)
         y = b["y"] if out is None else out
@@ -417,7 +445,7 @@ class MoeLayer:
 
     def decode(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, routing=None,
                ws=None, stream=None):
-        """One token through the fused single-launch decode path; returns the workspace."""
+        """One token through the batch-1 decode path (two launches); returns the workspace."""
         if ws is None:
             ws = _bytes_tensor(decode_workspace_bytes(self.H, self.I, self.I_sh, self.E, self.k),
                                self.device)

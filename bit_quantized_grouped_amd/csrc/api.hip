@@ -11,7 +11,7 @@ using namespace moeq4;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kMaxE = 1000;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -227,6 +227,19 @@ static int check_ws(const void* ws, size_t ws_bytes, size_t need) {
     return MOE_OK;
 }
 
+// One validated layer call: route, gate/up, down and combine in stream order.
+static int layer_call(const GemmProblem& p, const float* logits, void* route_ws, void* gemm_ws,
+                      uint16_t* y, hipStream_t stream) {
+    hipError_t e =
+        launch_route(logits, p.T, p.E, p.k, p.block_rows, p.max_blocks, p.r, route_ws, stream);
+    if (e == hipSuccess) e = launch_gateup(p, gemm_ws, stream);
+    if (e == hipSuccess) e = launch_down(p, gemm_ws, stream);
+    if (e == hipSuccess)
+        e = launch_combine(p.expert_out, p.shared_out, nullptr, p.r.assign_row, p.r.topk_w, p.T,
+                           p.H, p.k, y, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
                         int block_rows, const moe_routing* r, const moe_q4_mat* gate,
                         const moe_q4_mat* up, const moe_q4_mat* down, const moe_q4_mat* sh_gate,
@@ -243,6 +256,31 @@ int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E,
         hipError_t e = launch_gateup(p, ws, stream);
         if (e == hipSuccess) e = launch_down(p, ws, stream);
         return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_layer_q4(const uint16_t* x, const float* logits, int T, int H, int I, int I_sh, int E,
+                 int k, int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
+                 const moe_q4_mat* down, const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                 const moe_q4_mat* sh_down, const moe_routing* r, void* route_ws,
+                 size_t route_ws_bytes, uint16_t* expert_out, uint16_t* shared_out,
+                 void* gemm_ws, size_t gemm_ws_bytes, uint16_t* y, hipStream_t stream) {
+    try {
+        int st = gemm_args_ok(x, T, H, I, I_sh, E, k, block_rows, r, gate, up, down, sh_gate,
+                              sh_up, sh_down, expert_out, shared_out);
+        if (st) return st;
+        if (!logits || !y) return MOE_ERR_NULL;
+        if (!aligned(logits, 4) || !aligned(y, 16)) return MOE_ERR_ALIGN;
+        const size_t route_need = moe_route_workspace_bytes(T, E, k, block_rows);
+        if (route_need && (st = check_ws(route_ws, route_ws_bytes, route_need))) return st;
+        if ((st = check_ws(gemm_ws, gemm_ws_bytes,
+                           moe_gemm_workspace_bytes(T, H, I, I_sh, E, k, block_rows))))
+            return st;
+        const GemmProblem p = make_problem(x, T, H, I, I_sh, E, k, block_rows, r, gate, up, down,
+                                           sh_gate, sh_up, sh_down, expert_out, shared_out);
+        return layer_call(p, logits, route_ws, gemm_ws, y, stream);
     } catch (...) {
         return MOE_ERR_HIP;
     }
@@ -570,14 +608,11 @@ int moe_layer_chunked(const uint16_t* x, const float* logits, int T, int H, int 
         uint16_t* so = I_sh ? (uint16_t*)(base + L.shared_out) : nullptr;
         for (int t0 = 0; t0 < T; t0 += C) {
             const int Tc = (T - t0) < C ? (T - t0) : C;
-            st = moe_route(logits + (size_t)t0 * E, Tc, E, k, block_rows, &r, base + L.route_ws,
-                           L.route_bytes, stream);
-            if (st) return st;
-            st = moe_grouped_gemm_q4(x + (size_t)t0 * H, Tc, H, I, I_sh, E, k, block_rows, &r,
-                                     gate, up, down, sh_gate, sh_up, sh_down, eo, so,
-                                     base + L.gemm_ws, L.gemm_bytes, stream);
-            if (st) return st;
-            st = moe_combine(eo, so, &r, Tc, H, k, y + (size_t)t0 * H, stream);
+            const GemmProblem p = make_problem(x + (size_t)t0 * H, Tc, H, I, I_sh, E, k,
+                                               block_rows, &r, gate, up, down, sh_gate, sh_up,
+                                               sh_down, eo, so);
+            st = layer_call(p, logits + (size_t)t0 * E, base + L.route_ws, base + L.gemm_ws,
+                            y + (size_t)t0 * H, stream);
             if (st) return st;
         }
         return MOE_OK;

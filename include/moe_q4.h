@@ -154,6 +154,23 @@ int moe_grouped_gemm_q4(const uint16_t* x, int T, int H, int I, int I_sh, int E,
                         uint16_t* expert_out, uint16_t* shared_out,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* One whole layer call for T tokens: moe_route, moe_grouped_gemm_q4 and
+ * moe_combine in one entry point, enqueued in that order on `stream`, with
+ * the same arguments, buffers and results (routing r, expert_out,
+ * shared_out and y are written exactly as by those three calls; [P1]
+ * dothoosh.com "Prefill optimizations": GPU-resident routing feeding the
+ * fused grouped GEMM with no CPU sync between them).
+ *   route_ws: moe_route_workspace_bytes(T, E, k, block_rows) bytes (may be
+ *             NULL when that is 0); gemm_ws: moe_gemm_workspace_bytes(...)
+ *             bytes; both 256-byte aligned.  y bf16 [T, H], 16-byte aligned.
+ * Status codes as for the three calls. */
+int moe_layer_q4(const uint16_t* x, const float* logits, int T, int H, int I, int I_sh, int E,
+                 int k, int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
+                 const moe_q4_mat* down, const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                 const moe_q4_mat* sh_down, const moe_routing* r, void* route_ws,
+                 size_t route_ws_bytes, uint16_t* expert_out, uint16_t* shared_out,
+                 void* gemm_ws, size_t gemm_ws_bytes, uint16_t* y, hipStream_t stream);
+
 /* The two phases of moe_grouped_gemm_q4, for callers that schedule or time
  * them separately.  They share the workspace layout of moe_grouped_gemm_q4:
  * moe_expert_gateup_q4 writes the bf16 SwiGLU activations h (routed rows in

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert bq.abi_version() == 2
+    assert bq.abi_version() == 3
     for st, txt in [(0, "ok"), (-1, "null pointer"), (-2, "bad shape"), (-3, "misaligned pointer"),
                     (-4, "workspace too small"), (-5, "HIP launch error"), (-6, "unimplemented"),
                     (-99, "unknown status")]:
@@ -103,6 +103,35 @@ def test_gemm_rejects_bad_arguments():
     assert call(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
     nul = bq.MoeQ4Mat(FAKE.value, None, FAKE.value)
     assert call(mats=[m, nul, m, m, m, m]) == bq.MOE_ERR_NULL
+
+
+def test_layer_call_rejects_bad_arguments():
+    L = bq.lib()
+    r = _routing()
+    m = _mat()
+    ws = bq.gemm_workspace_bytes(64, 256, 128, 128, 16, 2, 32)
+
+    def call(x=FAKE, lg=FAKE, T=64, H=256, I=128, I_sh=128, E=16, k=2, br=32, mats=None,
+             rws=FAKE, rwsb=256, eo=FAKE, so=FAKE, gws=FAKE, wsb=ws, y=FAKE):
+        mats = mats or [m] * 6
+        args = [x, lg, T, H, I, I_sh, E, k, br]
+        args += [ctypes.byref(q) if q is not None else None for q in mats]
+        args += [ctypes.byref(r), rws, rwsb, eo, so, gws, wsb, y, None]
+        return L.moe_layer_q4(*args)
+
+    assert call(x=None) == bq.MOE_ERR_NULL
+    assert call(lg=None) == bq.MOE_ERR_NULL
+    assert call(y=None) == bq.MOE_ERR_NULL
+    assert call(gws=None) == bq.MOE_ERR_NULL
+    assert call(so=None) == bq.MOE_ERR_NULL
+    assert call(H=200) == bq.MOE_ERR_SHAPE
+    assert call(k=17) == bq.MOE_ERR_SHAPE
+    assert call(br=48) == bq.MOE_ERR_SHAPE
+    assert call(I_sh=0, so=None) == bq.MOE_ERR_SHAPE
+    assert call(lg=P(0x10002)) == bq.MOE_ERR_ALIGN
+    assert call(y=P(0x10008)) == bq.MOE_ERR_ALIGN
+    assert call(gws=P(0x10010)) == bq.MOE_ERR_ALIGN
+    assert call(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
 
 
 def test_combine_and_chunked_reject_bad_arguments():
