@@ -39,6 +39,8 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -97,6 +99,34 @@ def timed(fn, steps, warmup, torch):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / steps   # ms per call
+
+
+def read_ceiling(torch, bq, dev, nbytes=1 << 30, reps=20):
+    """HBM read ceiling in bytes/s: the library's streaming-read probe over a
+    buffer 4x the 256 MB Infinity Cache, timed back to back."""
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(bq.read_probe_sink_words(nbytes), dtype=torch.int32, device=dev)
+    ms = timed(lambda: bq.moe_read_probe(buf, sink), reps, 5, torch)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3)
+
+
+def device_facts(torch, dev):
+    props = torch.cuda.get_device_properties(dev)
+    facts = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+             "compute_units": props.multi_processor_count, "max_clock_mhz": None}
+    try:   # rocminfo lists the agent's peak engine clock
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        for block in out.split("Agent ")[1:]:
+            if "gfx950" in block:
+                m = re.search(r"Max Clock Freq\. \(MHz\):\s*(\d+)", block)
+                facts["max_clock_mhz"] = int(m.group(1)) if m else None
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return facts
 
 
 def kernel_src_sha():
@@ -240,6 +270,16 @@ def main():
     T = cfg.T
     ms = timed(lambda: layer.forward(x, lg), args.steps, args.warmup, torch)
     ms_cold = timed(cold(lambda L: L.forward(x, lg)), args.steps, args.warmup, torch)
+    # per-call durations (events around each call) for the median
+    per_call = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.forward(x, lg)
+        e1.record()
+        per_call.append((e0, e1))
+    torch.cuda.synchronize()
+    median_us = float(np.median([a.elapsed_time(b) for a, b in per_call])) * 1e3
     bufs = layer.buffers(T)
     counts = bufs["routing"].counts.cpu().numpy()
     touched = int(np.count_nonzero(counts))
@@ -274,6 +314,8 @@ def main():
     t_layer = ms * 1e-3
     t_roof = max(flops / MFMA_BF16_PEAK, layer_bytes / HBM_PEAK)
     achieved = gu_bytes / t_gu
+    ceiling = read_ceiling(torch, bq, dev)
+    log(f"measured HBM read ceiling: {ceiling/1e9:.0f} GB/s")
     result = {
         "metric": "MoE-layer tokens/s (prefill 512 tokens, 256 experts top-8 + shared, 4-bit g64)",
         "value": T / t_layer,
@@ -295,13 +337,17 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "grouped_q4_kernel gate/up+SwiGLU (moe_expert_gateup_q4)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": read_traffic(),
-                     "algorithmic_bytes": gu_bytes, "avg_launch_us": t_gu * 1e6},
+                     "algorithmic_bytes": gu_bytes, "avg_launch_us": t_gu * 1e6,
+                     "measured_read_ceiling": ceiling / 1e9,
+                     "frac_of_measured_ceiling": achieved / ceiling},
+        "device": device_facts(torch, dev),
         "layer": {"route_us": t_route * 1e6, "gateup_us": t_gu * 1e6, "down_us": t_dn * 1e6,
                   "combine_us": t_comb * 1e6, "touched_experts": touched,
                   "algorithmic_bytes": layer_bytes, "algorithmic_flops": flops,
                   "roofline_frac": t_roof / t_layer,
                   "mfma_frac": flops / t_layer / MFMA_BF16_PEAK,
                   "hbm_frac": layer_bytes / t_layer / HBM_PEAK,
+                  "median_us_per_call": median_us,
                   "cold_tokens_per_s": T / (ms_cold * 1e-3), "cold_us_per_call": ms_cold * 1e3,
                   "cold_hbm_frac": layer_bytes / (ms_cold * 1e-3) / HBM_PEAK},
     }
@@ -489,9 +535,13 @@ def main():
         t0 = time.perf_counter()
         oracle.moe_layer(xb, lgn, w.gate, w.up, w.down, cfg.k, w.sh_gate, w.sh_up, w.sh_down)
         dt = time.perf_counter() - t0
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in pools] or [1])
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
+                                 if p.get("user_api") == "blas"})) or None
         result["cpu_baseline"] = {
             "value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"one full 512-token layer call of the same workload ({dt:.1f} s; numpy fp64, "
                       f"BLAS threads {threads}, elementwise work single-threaded)"}
         log(f"cpu oracle: {dt:.1f} s for 512 tokens")

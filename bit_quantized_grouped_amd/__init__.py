@@ -75,6 +75,8 @@ _SIGNATURES = {
                                + [_P] * 4 + [_P, _S, _P]),
     "moe_expert_down_bf16": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
                              + [_P] * 2 + [_P, _P, _P, _S, _P]),
+    "moe_read_probe_sink_words": (_S, [_S]),
+    "moe_read_probe": (_I, [_P, _S, _P, _S, _P]),
     "moe_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_decode_q4": (_I, [_P, _P, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(MoeQ4Mat)] * 6
                       + [ctypes.POINTER(MoeRouting), _P, _P, _S, _P]),
@@ -315,6 +317,17 @@ def moe_router(x: torch.Tensor, w_router: torch.Tensor, logits: torch.Tensor, w_
     E = w_router.shape[0]
     _check(lib().moe_router(_ptr(x), T, H, _ptr(w_router), E, _ptr(w_gate), _ptr(logits),
                             _ptr(gate), _stream(stream, x.device)), "moe_router")
+
+
+def read_probe_sink_words(nbytes: int) -> int:
+    return lib().moe_read_probe_sink_words(nbytes)
+
+
+def moe_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Stream every byte of buf once; sink[i] = XOR of the uint32 words of 32 KB range i."""
+    _check(lib().moe_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                sink.numel() * sink.element_size() // 4,
+                                _stream(stream, buf.device)), "moe_read_probe")
 
 
 def decode_workspace_bytes(H, I, I_sh, E, k) -> int:

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmoe_q4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
-SOURCES = ["api.hip", "route.hip", "gemm_q4.hip", "combine.hip", "decode.hip", "dequant.hip", "router.hip"]
+SOURCES = ["api.hip", "route.hip", "gemm_q4.hip", "combine.hip", "decode.hip", "dequant.hip", "router.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -491,6 +491,22 @@ int moe_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
     }
 }
 
+size_t moe_read_probe_sink_words(size_t bytes) { return read_probe_sink_words(bytes); }
+
+int moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                   hipStream_t stream) {
+    try {
+        if (!buf || !sink) return MOE_ERR_NULL;
+        if (bytes < 16 || bytes % 16 || bytes / 16 > ((size_t)1 << 40)) return MOE_ERR_SHAPE;
+        if (!aligned(buf, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGN;
+        if (sink_words < read_probe_sink_words(bytes)) return MOE_ERR_WORKSPACE;
+        if (read_probe_sink_words(bytes) > 0x7fffffffu) return MOE_ERR_SHAPE;
+        return launch_read_probe(buf, bytes, sink, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k) {
     if (check_layer_shape(1, H, I, I_sh, E, k, 32) || k > 64) return 0;
     return decode_ws_layout(I, I_sh, k, nullptr, nullptr);

@@ -82,6 +82,10 @@ hipError_t launch_combine(const uint16_t* expert_out, const uint16_t* shared_out
                           const float* shared_w, const int32_t* assign_row, const float* topk_w,
                           int T, int H, int k, uint16_t* y, hipStream_t stream);
 
+// probe.hip: streaming-read probe, one sink word per 32 KB read
+size_t read_probe_sink_words(size_t bytes);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // router.hip
 hipError_t launch_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
                          const uint16_t* w_gate, float* logits, float* gate, hipStream_t stream);

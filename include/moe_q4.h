@@ -264,6 +264,21 @@ int moe_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
 int moe_q4_prepack(const uint32_t* src_codes, int n_exp, int N, int K, uint32_t* dst_codes,
                    hipStream_t stream);
 
+/* Streaming-read probe (measurement only): reads `bytes` of `buf` once with
+ * 16-byte loads, one contiguous 32 KB range per workgroup, and writes the
+ * XOR of range i's 32-bit words to sink[i] (a range past the end of buf is
+ * shortened; its missing words count as zero).  Timing it over a buffer
+ * larger than the 256 MB Infinity Cache gives the HBM read ceiling that the
+ * weight-streaming kernels are compared against, next to the published
+ * peak.
+ *   buf: device, 16-byte aligned, bytes a positive multiple of 16
+ *   sink: device, moe_read_probe_sink_words(bytes) uint32 words or more
+ * Status: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE (sink
+ * too short), MOE_ERR_HIP. */
+size_t moe_read_probe_sink_words(size_t bytes);
+int moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                   hipStream_t stream);
+
 /* Device workspace bytes moe_decode_q4 needs (0 on bad shapes). */
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k);
 

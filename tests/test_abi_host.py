@@ -134,6 +134,22 @@ def test_layer_call_rejects_bad_arguments():
     assert call(wsb=ws - 1) == bq.MOE_ERR_WORKSPACE
 
 
+def test_read_probe_sizes_and_bad_arguments():
+    L = bq.lib()
+    assert bq.read_probe_sink_words(16) == 1
+    assert bq.read_probe_sink_words(32768) == 1
+    assert bq.read_probe_sink_words(32768 + 16) == 2
+    assert bq.read_probe_sink_words(1 << 30) == (1 << 30) // 32768
+    sink_ok = 1 << 20
+    assert L.moe_read_probe(None, 1 << 20, FAKE, sink_ok, None) == bq.MOE_ERR_NULL
+    assert L.moe_read_probe(FAKE, 1 << 20, None, sink_ok, None) == bq.MOE_ERR_NULL
+    for nbytes in (0, 8, 24, 1000):
+        assert L.moe_read_probe(FAKE, nbytes, FAKE, sink_ok, None) == bq.MOE_ERR_SHAPE
+    assert L.moe_read_probe(P(0x10008), 1 << 20, FAKE, sink_ok, None) == bq.MOE_ERR_ALIGN
+    assert L.moe_read_probe(FAKE, 1 << 20, P(0x10002), sink_ok, None) == bq.MOE_ERR_ALIGN
+    assert L.moe_read_probe(FAKE, 1 << 20, FAKE, 31, None) == bq.MOE_ERR_WORKSPACE
+
+
 def test_combine_and_chunked_reject_bad_arguments():
     L = bq.lib()
     r = _routing()
