@@ -93,3 +93,26 @@ def test_route_exact_counts(counts):
     got = gpu_route(L, 1, 32)
     assert got["counts"].tolist() == counts
     assert_routing_matches(got, L, 1, 32)
+
+
+# Property-based cases (hypothesis, derandomized so every run draws the same
+# examples): random shapes, logits drawn from a few levels so ties are common,
+# some signed zeros, every block height; the routing arrays must match the
+# oracle bit for bit.
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(T=st.integers(1, 300), E=st.integers(1, 320), kq=st.floats(0.0, 1.0),
+       levels=st.integers(1, 6), zeros=st.booleans(), br=st.sampled_from([16, 32, 64]),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_route_property_random_ties(T, E, kq, levels, zeros, br, seed):
+    k = 1 + int(kq * (min(E, 64) - 1))
+    rng = np.random.default_rng(seed)
+    logits = (rng.integers(0, levels, (T, E)) - levels // 2).astype(np.float32) * np.float32(0.75)
+    if zeros:   # a mix of +0.0 and -0.0 where the level is zero
+        neg = rng.random((T, E)) < 0.5
+        logits[(logits == 0) & neg] = np.float32(-0.0)
+    announce(f"route property T={T} E={E} k={k} levels={levels} zeros={zeros} br={br} seed={seed}")
+    assert_routing_matches(gpu_route(logits, k, br), logits, k, br)
