@@ -184,17 +184,18 @@ def sweep(args, torch, bq, dev):
     from workload import CONFIGS, make_activations, make_weights
     cfg = CONFIGS["prefill512"]
     w = make_weights(cfg, seed=0)
-    base = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev)
+    base = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, prepack=True)
     mats = base.weight_mats()
     out = {"sweep": "block_rows x prefill, chunk_tokens x skewed prefill", "unit": "tokens/s",
-           "block_rows": {}, "chunk_tokens": {}}
+           "code_layout": "tile-packed", "warmup": args.warmup, "block_rows": {},
+           "chunk_tokens": {}}
     for name in ("prefill512", "prefill2048"):
         c = CONFIGS[name]
         xb, lgn = make_activations(c)
         x, lg = bq.bf16_from_bits(xb, dev), torch.from_numpy(lgn).to(dev)
         for br in (16, 32, 64):
             L = bq.MoeLayer.from_device(mats, c.H, c.I, c.I_sh, c.E, c.k, dev, block_rows=br)
-            ms = timed(lambda: L.forward(x, lg), max(20, args.steps // 4), 5, torch)
+            ms = timed(lambda: L.forward(x, lg), max(20, args.steps // 4), args.warmup, torch)
             out["block_rows"].setdefault(name, {})[br] = c.T / (ms * 1e-3)
             log(f"sweep {name} block_rows {br}: {ms*1e3:.1f} us/call")
             del L
@@ -204,7 +205,8 @@ def sweep(args, torch, bq, dev):
     y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
     for chunk in (512, 1024, 2048, 4096):
         ws = base.forward_chunked(x, lg, chunk, y)
-        ms = timed(lambda: base.forward_chunked(x, lg, chunk, y, ws), 10, 2, torch)
+        ms = timed(lambda: base.forward_chunked(x, lg, chunk, y, ws), 10,
+                   max(2, args.warmup // 40), torch)
         out["chunk_tokens"][chunk] = c.T / (ms * 1e-3)
         log(f"sweep skew8192 chunk {chunk}: {ms*1e3:.1f} us per 8192 tokens")
         del ws
