@@ -11,10 +11,10 @@
 //     0 also publishes it), then its waves stream gate/up weight rows of the
 //     k chosen experts and the shared expert, kGuRows row pairs per wave at a
 //     time, and write h = bf16(silu(g) * u).
-//   decode_down_kernel: each workgroup owns 4 output columns; its 4 waves
+//   decode_down_kernel: each workgroup owns 4 output columns; its 8 waves
 //     split the experts, stream those experts' down-projection rows for the
 //     4 columns, and weight each expert's dot with topk_w (shared expert:
-//     weight 1); the 4 wave partials are summed in a fixed order, y = bf16.
+//     weight 1); the wave partials are summed in a fixed order, y = bf16.
 //
 // The weights are 4-bit groupwise affine, w = q * s + b per 64 weights ([P1]
 // "Prefill optimizations", fused-dequantization bullet; [P3] "A big model
@@ -45,6 +45,13 @@ constexpr int kDecMaxK = 64;
 constexpr int kGuRows = MOE_DEC_GU_ROWS;   // gate/up row pairs one wave streams together
 constexpr int kDnExp = MOE_DEC_DN_EXP;     // experts whose down rows one wave loads together
 constexpr int kDnCols = 4;    // output columns per down workgroup (16 lanes each)
+#ifndef MOE_DEC_DN_WAVES
+#define MOE_DEC_DN_WAVES 8
+#endif
+// waves of a down workgroup; they split the k + 1 experts, so with 8 waves and
+// k = 8 only one wave streams two experts (8 beat 4 by 0.8 us per token, 12 tied, 16 lost)
+constexpr int kDnWaves = MOE_DEC_DN_WAVES;
+constexpr int kDnThreads = kDnWaves * WAVE;
 
 // q * 2^-9 for the 8 codes of a packed word, in code order (low nibble first).
 __device__ __forceinline__ void codes_unit(uint32_t w, float (&q)[8]) {
@@ -232,8 +239,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
     }
 }
 
-__global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) {
-    __shared__ float s_part[kDecWaves][kDnCols];
+__global__ __launch_bounds__(kDnThreads) void decode_down_kernel(DecodeArgs p) {
+    __shared__ float s_part[kDnWaves][kDnCols];
     const int tid = threadIdx.x, lane = tid % WAVE;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int k = p.k, H = p.H, I = p.I, I_sh = p.I_sh;
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) 
     const int kl = (lane % 16) * 32;
     const float unit_inv = 1.0f / fp8_unit();
     float acc = 0.0f;
-    for (int j0 = wave; j0 < nexp; j0 += kDecWaves * kDnExp) {
+    for (int j0 = wave; j0 < nexp; j0 += kDnWaves * kDnExp) {
         const uint32_t* dc[kDnExp];
         const uint16_t *ds[kDnExp], *db[kDnExp];
         const uint16_t* hp[kDnExp];
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) 
         int N[kDnExp];
 #pragma unroll
         for (int i = 0; i < kDnExp; ++i) {
-            const int j = j0 + i * kDecWaves;
+            const int j = j0 + i * kDnWaves;
             const bool on = j < nexp;
             const bool sh = j == k;
             const int e = on && !sh ? p.sel_idx[j] : 0;
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs p) 
     if (tid < kDnCols) {
         float y = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kDecWaves; ++w) y += s_part[w][tid];
+        for (int w = 0; w < kDnWaves; ++w) y += s_part[w][tid];
         p.y[blockIdx.x * kDnCols + tid] = __builtin_bit_cast(uint16_t, (__bf16)y);
     }
 }
@@ -328,7 +335,7 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
 #undef MOE_DECODE_GU
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_down_kernel, dim3(args.H / kDnCols), dim3(kDecThreads), 0, stream,
+    hipLaunchKernelGGL(decode_down_kernel, dim3(args.H / kDnCols), dim3(kDnThreads), 0, stream,
                        args);
     return hipGetLastError();
 }
