@@ -79,6 +79,7 @@ SMALL = [
     (130, 384, 192, 12, 2, 320, 64),      # K not a multiple of 256; I_sh != I
     (1, 2048, 512, 256, 8, 512, 32),      # batch-1 decode shape
     (9, 128, 64, 4, 4, 64, 16),           # k = E
+    (50, 64, 64, 1000, 20, 64, 32),       # smallest H and I, largest E, k > 16 (radix top-k)
 ]
 
 
@@ -97,6 +98,27 @@ def test_small_layer_parity(T, H, I, E, k, I_sh, br):
     if I_sh:
         ok, ratio = tol_ok(bf16_bits_to_f64(got["shared_out"]), ref["shared_out"])
         assert ok, f"shared_out {ratio:.3f}"
+    assert_close_layer(got["y"], ref["y"])
+
+
+def test_one_expert_takes_every_token():
+    """Expert 3's logit is raised for every token: it gets all T rows (10 full
+    32-row blocks and a ragged 11th), the second choices spread over the rest,
+    and several experts stay empty."""
+    T, H, I, E, k, I_sh = 330, 256, 128, 16, 2, 128
+    cfg = small_config(T, H, I, E, k, I_sh, seed=77)
+    w = make_weights(cfg, seed=78, cache=False)
+    x_bits, logits = make_activations(cfg)
+    logits = logits.copy()
+    logits[:, 3] += np.float32(50.0)
+    logits[:, 8:] -= np.float32(50.0)      # experts 8..15 never chosen
+    announce("one expert takes every token")
+    layer = bq.MoeLayer(w, H, I, I_sh, E, k, DEV)
+    got = run_layer(layer, x_bits, logits)
+    assert int(got["routing"]["counts"][3]) == T
+    assert np.all(got["routing"]["counts"][8:] == 0)
+    ref = oracle_layer(w, cfg, x_bits, logits)
+    assert_routing_matches(got["routing"], logits, k)
     assert_close_layer(got["y"], ref["y"])
 
 
