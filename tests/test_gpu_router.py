@@ -53,6 +53,8 @@ def _check_logits(got, x_bits, wr_bits):
     (1, 2048, 256, True),       # batch-1 decode
     (37, 384, 100, False),      # ragged T, E not a multiple of 16
     (16, 64, 1000, True),       # smallest H, largest E
+    (1000, 256, 100, False),    # 32 x 32 tiles: ragged T and E
+    (384, 128, 31, True),       # first size on 32 x 32 tiles; E + gate = one row tile
 ])
 def test_router_logits_and_gate(T, H, E, gated):
     cfg = small_config(T, H, 64, E, 1, 0, seed=T + E)
