@@ -153,7 +153,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int k = p.k, H = p.H, I = p.I, I_sh = p.I_sh;
 
-    if (wave == 0)
+    // One pass of the grid covers every task, so this workgroup's rows are
+    // tasks [8b, 8b + 8): when they are all shared-expert rows it needs no
+    // top-k (workgroup 0 still computes it to publish the selection).
+    const bool need_topk =
+        blockIdx.x == 0 || (int)(blockIdx.x + 1) * kDecWaves * kGuRows > I_sh;
+    if (wave == 0 && need_topk)
         topk_token<EPL>(p.logits, p.E, k, s_idx, s_w, s_scr, (int*)(s_scr + k),
                         (float*)(s_scr + 2 * k), nullptr);
     __syncthreads();
