@@ -117,8 +117,8 @@ const char* moe_status_str(int status);
  * block_expert / block_row.  Returns a negative status on bad shapes. */
 int moe_route_max_blocks(int T, int E, int k, int block_rows);
 
-/* Device workspace bytes moe_route needs (0 on bad shapes; this build needs
- * none for valid shapes, and then ws may be NULL). */
+/* Device workspace bytes moe_route needs (0 on bad shapes; the routing
+ * kernels need none for valid shapes, and then ws may be NULL). */
 size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows);
 
 /* GPU-resident routing ([P1] "Prefill optimizations", GPU-resident routing
