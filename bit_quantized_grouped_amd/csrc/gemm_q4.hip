@@ -446,6 +446,191 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     }
 }
 
+// ---- Down projection over whole-K tiles (K = I <= 512) ----
+// Work item = one row block (<= 32 rows) x CG = WAVES * TPW * 32 output
+// columns.  The block's h rows (32 x K bf16) are staged in LDS once per item
+// and every wave reads them; each wave owns TPW tiles of 32 output columns
+// over the whole K and requests all of their code words before staging h,
+// so the item streams its weights in one round of loads.  The product is
+// v_mfma_f32_32x32x16_bf16: lane half hf (lane / 32) takes the words of the
+// second half of K when hf = 1, so each lane reads half a weight row (K / 4
+// bytes) contiguously and its A elements come from the same K positions.
+// The dequantization and its arithmetic are those of grouped_q4_kernel
+// (dequant_word), so both kernels produce the same weights.
+template <int KW, int TPW, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, int br) {
+    constexpr int K = KW * 64;            // weights per row (the down K = I)
+    constexpr int NT = WAVES * 64;
+    constexpr int LDH = K + 8;            // h row stride in LDS, elements
+    constexpr int G = KW;                 // scale groups per weight row
+    constexpr int GS = G + 2;             // scale row stride in LDS, elements
+    constexpr int CG = WAVES * TPW * 32;  // output columns per item
+    constexpr int CGS = CG + 8;           // output tile row stride in LDS
+    constexpr int WPL = 4 * KW;           // code words per lane per tile (half a row)
+    constexpr int NGL = KW >= 2 ? KW / 2 : 1;   // scale groups per lane per tile
+    static_assert(WAVES % 2 == 0, "tile-packed offsets assume 64-row steps per tile round");
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem_d[];
+    uint16_t* sH = smem_d;                // [32][LDH]
+    uint16_t* sSc = sH + 32 * LDH;        // [CG][GS]
+    uint16_t* sBi = sSc + CG * GS;        // [CG][GS]
+    uint16_t* sO = smem_d;                // [32][CGS], after the math (aliases sH)
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int n = lane & 31, hf = lane >> 5;
+
+    const int n_items = (p.sh_blocks + p.n_blocks[0]) * p.n_tiles;
+    const int per = (n_items + kXcds - 1) / kXcds;
+    const int xcd = blockIdx.x % kXcds, seq = blockIdx.x / kXcds;
+    const int item = xcd * per + seq;
+    if (seq >= per || item >= n_items) return;
+    const int slot = item / p.n_tiles, grp = item % p.n_tiles;
+    const bool is_sh = slot < p.sh_blocks;
+    int r0, nr, expert = 0;
+    if (is_sh) {
+        r0 = slot * br;
+        nr = min(br, p.T - r0);
+    } else {
+        const int b = slot - p.sh_blocks;
+        expert = p.block_expert[b];
+        r0 = p.block_row[b];
+        nr = min(br, p.offsets[expert + 1] - r0);
+    }
+    const int N = is_sh ? p.N_sh : p.N;
+    const int n_base = grp * CG;
+    if (n_base >= N) return;   // uniform per workgroup
+    const uint16_t* A = is_sh ? p.a_shared : p.a_routed;
+    const int lda = is_sh ? p.lda_shared : p.lda_routed;
+    const int a_rows = is_sh ? p.rows_shared : p.rows_routed;
+    uint16_t* out = is_sh ? p.out_shared : p.out_routed;
+    const QMatDev& q = is_sh ? p.sB[0] : p.rB[0];
+    const size_t rows0 = (size_t)expert * N;
+
+    // ---- all code words of the wave's TPW tiles ----
+    // Tile i of this wave covers output columns n_base + (i*WAVES + wave)*32 ..+32;
+    // lane (n, hf) reads words hf*WPL .. +WPL of row (column) n of the tile,
+    // KW loads of 4 words.  The per-(tile, load) step is uniform in both word
+    // orders and rides in the scalar offset; tiles past N are requested
+    // outside the buffer resource (zeros, no memory access).
+    const rsrc_t rc = make_rsrc(q.codes + rows0 * (K / 8), (uint32_t)N * (K / 2));
+    const int layout = q.layout;
+    const int voff = (int)code_word(layout, (uint32_t)(n_base + wave * 32 + n), (uint32_t)(hf * WPL),
+                                    (uint32_t)K) * 4;
+    u32x4_t Bq[TPW][KW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const bool ok = n_base + (i * WAVES + wave) * 32 < N;
+        const int vo = voff + (ok ? 0 : kVoffOob);
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+            const int so = layout == 0
+                               ? i * WAVES * 32 * (K / 2) + 16 * j
+                               : i * (WAVES / 2) * (K / 64) * 2048 + (KW >= 2 ? (j / 2) * 2048 + (j % 2) * 16 : 0);
+            Bq[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, 0));
+        }
+    }
+
+    // ---- h rows of the block (contiguous; padding rows repeat the last row) ----
+    constexpr int HPIECES = 32 * (K / 8);
+    constexpr int HPT = (HPIECES + NT - 1) / NT;
+    const rsrc_t ra = make_rsrc(A, (uint32_t)a_rows * lda * 2);
+    u32x4_t hv[HPT];
+#pragma unroll
+    for (int t = 0; t < HPT; ++t) {
+        const int qq = tid + NT * t;
+        if (HPIECES % NT == 0 || qq < HPIECES) {
+            const int row = qq / (K / 8), c8 = qq % (K / 8);
+            hv[t] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                             ra, (r0 + min(row, nr - 1)) * lda * 2 + c8 * 16, 0, 0));
+        }
+    }
+    // ---- scales and biases of the item's CG rows (rows past N read as zero) ----
+    {
+        const rsrc_t rs = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
+        const rsrc_t rb = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
+        constexpr int SP = CG * G / 8;
+        for (int pc = tid; pc < SP; pc += NT) {
+            const int vo = (n_base * G + pc * 8) * 2;
+            const u32x4_t vs = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+            const u32x4_t vb = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, vo, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int flat = pc * 8 + e;
+                const int row = flat / G, g = flat % G;
+                sSc[row * GS + g] = (uint16_t)(vs[e / 2] >> (16 * (e & 1)));
+                sBi[row * GS + g] = (uint16_t)(vb[e / 2] >> (16 * (e & 1)));
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < HPT; ++t) {
+        const int qq = tid + NT * t;
+        if (HPIECES % NT == 0 || qq < HPIECES) {
+            const int row = qq / (K / 8), c8 = qq % (K / 8);
+            *(u32x4_t*)(sH + row * LDH + c8 * 8) = hv[t];
+        }
+    }
+    __syncthreads();
+
+    // ---- math: per tile, WPL words per lane, one MFMA per word ----
+    const float unit_inv = 1.0f / fp8_unit();
+    const int c0 = hf * WPL;              // lane's first word in the row
+    f32x16_t acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+        if (n_base + (i * WAVES + wave) * 32 >= N) continue;   // uniform per wave
+        const int col = (i * WAVES + wave) * 32 + n;            // within the item
+        float sc[NGL], bi[NGL];
+#pragma unroll
+        for (int gg = 0; gg < NGL; ++gg) {
+            const int gi = c0 / 8 + gg;
+            sc[gg] = bf16_to_f32(sSc[col * GS + gi]) * unit_inv;
+            bi[gg] = bf16_to_f32(sBi[col * GS + gi]);
+        }
+#pragma unroll
+        for (int j = 0; j < KW; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int gl = KW >= 2 ? j / 2 : 0;
+                const bf16x8_t bw = dequant_word(Bq[i][j][w], sc[gl], bi[gl]);
+                const bf16x8_t a = *(const bf16x8_t*)(sH + n * LDH + (c0 + 4 * j + w) * 8);
+                acc[i] = mfma_32x32x16(a, bw, acc[i]);
+            }
+    }
+
+    // ---- epilogue: bf16 tile [32][CG] in LDS (over sH), then 16-byte row stores ----
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int col = (i * WAVES + wave) * 32 + n;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = 8 * (e / 4) + 4 * hf + (e % 4);
+            sO[row * CGS + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][e]);
+        }
+    }
+    __syncthreads();
+    constexpr int OPIECES = 32 * CG / 8;
+    const int ncols = min(CG, N - n_base);
+    for (int qq = tid; qq < OPIECES; qq += NT) {
+        const int row = qq / (CG / 8), c8 = (qq % (CG / 8)) * 8;
+        if (row < nr && c8 < ncols)
+            *(u32x4_t*)(out + (size_t)(r0 + row) * N + n_base + c8) =
+                *(const u32x4_t*)(sO + row * CGS + c8);
+    }
+}
+
+template <int KW, int TPW, int WAVES>
+static size_t down_tiles_lds_bytes() {
+    constexpr int K = KW * 64, CG = WAVES * TPW * 32;
+    const size_t a = (size_t)32 * (K + 8) * 2 + (size_t)2 * CG * (KW + 2) * 2;
+    const size_t o = (size_t)32 * (CG + 8) * 2;
+    return a > o ? a : o;
+}
+
 // Dynamic LDS bytes of one grouped_q4_kernel instance for K-groups G.
 template <int NMAT, int MT, int KC, int NSUB, int WAVES>
 static size_t grouped_lds_bytes(int G, int wg_per_cu) {
@@ -567,8 +752,45 @@ hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
     return hipGetLastError();
 }
 
+#ifndef MOE_DT_WAVES
+#define MOE_DT_WAVES 4
+#endif
+#ifndef MOE_DT_TPW
+#define MOE_DT_TPW 2
+#endif
+
+template <int KW>
+static void launch_down_tiles(GroupedArgs a, int br, int n_max, int slots, hipStream_t stream) {
+    constexpr int cg = MOE_DT_WAVES * MOE_DT_TPW * 32;
+    a.n_tiles = (n_max + cg - 1) / cg;
+    const long long items = (long long)slots * a.n_tiles;
+    const int grid = (int)((items + kXcds - 1) / kXcds) * kXcds;
+    down_tiles_kernel<KW, MOE_DT_TPW, MOE_DT_WAVES>
+        <<<grid, MOE_DT_WAVES * 64, down_tiles_lds_bytes<KW, MOE_DT_TPW, MOE_DT_WAVES>(), stream>>>(a, br);
+}
+
+// The whole-K tile kernel serves row blocks of up to 32 rows with one K
+// (routed and shared) of 64, 128, 256 or 512; other shapes take the
+// K-chunked grouped kernel.
+static bool down_tiles_fits(const GemmProblem& p) {
+#ifdef MOE_DT_DISABLE
+    return false;
+#endif
+    if (p.block_rows > 32) return false;
+    if (p.I_sh && p.I_sh != p.I) return false;
+    return p.I == 64 || p.I == 128 || p.I == 256 || p.I == 512;
+}
+
 hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream) {
     const GroupedArgs a = down_args(p, ws);
+    if (down_tiles_fits(p)) {
+        const int slots = a.sh_blocks + p.max_blocks;
+        if (p.I == 512) launch_down_tiles<8>(a, p.block_rows, p.H, slots, stream);
+        else if (p.I == 256) launch_down_tiles<4>(a, p.block_rows, p.H, slots, stream);
+        else if (p.I == 128) launch_down_tiles<2>(a, p.block_rows, p.H, slots, stream);
+        else launch_down_tiles<1>(a, p.block_rows, p.H, slots, stream);
+        return hipGetLastError();
+    }
     launch_grouped<1, MOE_DN_NSUB, MOE_DN_DEPTH, MOE_DN_WAVES>(
         a, p.block_rows, pick_kc(p.I, p.I_sh, MOE_DN_KC), p.H, a.sh_blocks + p.max_blocks,
         (p.I > p.I_sh ? p.I : p.I_sh) / 64, MOE_DN_WG_PER_CU, stream);

@@ -11,6 +11,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -71,6 +72,15 @@ __device__ __forceinline__ uint32_t code_word(int layout, uint32_t n, uint32_t c
 // it holds D[4*(l/16) + i][l%16], i = 0..3.
 __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l%32]; it
+// holds D[8*(i/4) + 4*(l/32) + i%4][l%32], i = 0..15.  Only the pairing of A
+// and B elements along K matters: a caller may assign each lane's 8 K
+// positions freely as long as its A and B elements follow the same order.
+__device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp each).
