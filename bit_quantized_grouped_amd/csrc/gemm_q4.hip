@@ -506,7 +506,39 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     const QMatDev& q = is_sh ? p.sB[0] : p.rB[0];
     const size_t rows0 = (size_t)expert * N;
 
-    // ---- all code words of the wave's TPW tiles ----
+    // ---- h rows of the block (contiguous; padding rows repeat the last row) ----
+    constexpr int HPIECES = 32 * (K / 8);
+    constexpr int HPT = (HPIECES + NT - 1) / NT;
+    const rsrc_t ra = make_rsrc(A, (uint32_t)a_rows * lda * 2);
+    u32x4_t hv[HPT];
+#pragma unroll
+    for (int t = 0; t < HPT; ++t) {
+        const int qq = tid + NT * t;
+        if (HPIECES % NT == 0 || qq < HPIECES) {
+            const int row = qq / (K / 8), c8 = qq % (K / 8);
+            hv[t] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                             ra, (r0 + min(row, nr - 1)) * lda * 2 + c8 * 16, 0, 0));
+        }
+    }
+    // ---- scales and biases of the item's CG rows (rows past N read as zero) ----
+    constexpr int SP = CG * G / 8;                  // 16-byte pieces per array
+    constexpr int SPT = (SP + NT - 1) / NT;
+    const rsrc_t rs = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
+    const rsrc_t rb = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
+    u32x4_t vs[SPT], vb[SPT];
+#pragma unroll
+    for (int t = 0; t < SPT; ++t) {
+        const int pc = tid + NT * t;
+        if (SP % NT == 0 || pc < SP) {
+            const int vo = (n_base * G + pc * 8) * 2;
+            vs[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+            vb[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, vo, 0, 0));
+        }
+    }
+    // ---- all code words of the wave's TPW tiles, requested after the h rows and
+    // scales so that the h stores below wait only for those; tile 0's math then
+    // starts while tile 1's words are still arriving ----
     // Tile i of this wave covers output columns n_base + (i*WAVES + wave)*32 ..+32;
     // lane (n, hf) reads words hf*WPL .. +WPL of row (column) n of the tile,
     // KW loads of 4 words.  The per-(tile, load) step is uniform in both word
@@ -530,36 +562,16 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
         }
     }
 
-    // ---- h rows of the block (contiguous; padding rows repeat the last row) ----
-    constexpr int HPIECES = 32 * (K / 8);
-    constexpr int HPT = (HPIECES + NT - 1) / NT;
-    const rsrc_t ra = make_rsrc(A, (uint32_t)a_rows * lda * 2);
-    u32x4_t hv[HPT];
 #pragma unroll
-    for (int t = 0; t < HPT; ++t) {
-        const int qq = tid + NT * t;
-        if (HPIECES % NT == 0 || qq < HPIECES) {
-            const int row = qq / (K / 8), c8 = qq % (K / 8);
-            hv[t] = __builtin_bit_cast(
-                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                             ra, (r0 + min(row, nr - 1)) * lda * 2 + c8 * 16, 0, 0));
-        }
-    }
-    // ---- scales and biases of the item's CG rows (rows past N read as zero) ----
-    {
-        const rsrc_t rs = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
-        const rsrc_t rb = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
-        constexpr int SP = CG * G / 8;
-        for (int pc = tid; pc < SP; pc += NT) {
-            const int vo = (n_base * G + pc * 8) * 2;
-            const u32x4_t vs = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
-            const u32x4_t vb = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, vo, 0, 0));
+    for (int t = 0; t < SPT; ++t) {
+        const int pc = tid + NT * t;
+        if (SP % NT == 0 || pc < SP) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int flat = pc * 8 + e;
                 const int row = flat / G, g = flat % G;
-                sSc[row * GS + g] = (uint16_t)(vs[e / 2] >> (16 * (e & 1)));
-                sBi[row * GS + g] = (uint16_t)(vb[e / 2] >> (16 * (e & 1)));
+                sSc[row * GS + g] = (uint16_t)(vs[t][e / 2] >> (16 * (e & 1)));
+                sBi[row * GS + g] = (uint16_t)(vb[t][e / 2] >> (16 * (e & 1)));
             }
         }
     }
