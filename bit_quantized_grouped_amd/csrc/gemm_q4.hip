@@ -457,7 +457,11 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
 // bytes) contiguously and its A elements come from the same K positions.
 // The dequantization and its arithmetic are those of grouped_q4_kernel
 // (dequant_word), so both kernels produce the same weights.
-template <int KW, int TPW, int WAVES>
+// MT = 64 pairs the row blocks of the 32-row map: block 2i of an expert (counted
+// from its first block) takes its own rows and those of block 2i+1, which
+// exits at once; the shared expert is cut into 64-row slots (sh_blocks set for
+// 64 rows by the host).
+template <int KW, int TPW, int WAVES, int MT = 32>
 __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, int br) {
     constexpr int K = KW * 64;            // weights per row (the down K = I)
     constexpr int NT = WAVES * 64;
@@ -468,12 +472,13 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     constexpr int CGS = CG + 8;           // output tile row stride in LDS
     constexpr int WPL = 4 * KW;           // code words per lane per tile (half a row)
     constexpr int NGL = KW >= 2 ? KW / 2 : 1;   // scale groups per lane per tile
+    constexpr int MR = MT / 32;           // 32-row MFMA tiles per item
     static_assert(WAVES % 2 == 0, "tile-packed offsets assume 64-row steps per tile round");
     extern __shared__ __attribute__((aligned(16))) uint16_t smem_d[];
-    uint16_t* sH = smem_d;                // [32][LDH]
-    uint16_t* sSc = sH + 32 * LDH;        // [CG][GS]
+    uint16_t* sH = smem_d;                // [MT][LDH]
+    uint16_t* sSc = sH + MT * LDH;        // [CG][GS]
     uint16_t* sBi = sSc + CG * GS;        // [CG][GS]
-    uint16_t* sO = smem_d;                // [32][CGS], after the math (aliases sH)
+    uint16_t* sO = smem_d;                // [MT][CGS], after the math (aliases sH)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -488,13 +493,14 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     const bool is_sh = slot < p.sh_blocks;
     int r0, nr, expert = 0;
     if (is_sh) {
-        r0 = slot * br;
-        nr = min(br, p.T - r0);
+        r0 = slot * MT;
+        nr = min(MT, p.T - r0);
     } else {
         const int b = slot - p.sh_blocks;
         expert = p.block_expert[b];
         r0 = p.block_row[b];
-        nr = min(br, p.offsets[expert + 1] - r0);
+        if (MT > br && ((r0 - p.offsets[expert]) / br) % (MT / br) != 0) return;   // a follower
+        nr = min(MT, p.offsets[expert + 1] - r0);
     }
     const int N = is_sh ? p.N_sh : p.N;
     const int n_base = grp * CG;
@@ -507,7 +513,7 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     const size_t rows0 = (size_t)expert * N;
 
     // ---- h rows of the block (contiguous; padding rows repeat the last row) ----
-    constexpr int HPIECES = 32 * (K / 8);
+    constexpr int HPIECES = MT * (K / 8);
     constexpr int HPT = (HPIECES + NT - 1) / NT;
     const rsrc_t ra = make_rsrc(A, (uint32_t)a_rows * lda * 2);
     u32x4_t hv[HPT];
@@ -588,11 +594,14 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     // ---- math: per tile, WPL words per lane, one MFMA per word ----
     const float unit_inv = 1.0f / fp8_unit();
     const int c0 = hf * WPL;              // lane's first word in the row
-    f32x16_t acc[TPW];
+    const int mr_act = (nr + 31) / 32;    // 32-row tiles holding rows of this item
+    f32x16_t acc[TPW][MR];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][r][e] = 0.f;
         if (n_base + (i * WAVES + wave) * 32 >= N) continue;   // uniform per wave
         const int col = (i * WAVES + wave) * 32 + n;            // within the item
         float sc[NGL], bi[NGL];
@@ -608,8 +617,13 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
             for (int w = 0; w < 4; ++w) {
                 const int gl = KW >= 2 ? j / 2 : 0;
                 const bf16x8_t bw = dequant_word(Bq[i][j][w], sc[gl], bi[gl]);
-                const bf16x8_t a = *(const bf16x8_t*)(sH + n * LDH + (c0 + 4 * j + w) * 8);
-                acc[i] = mfma_32x32x16(a, bw, acc[i]);
+#pragma unroll
+                for (int r = 0; r < MR; ++r) {
+                    if (r > 0 && r >= mr_act) break;   // 32-row tiles past the item's rows
+                    const bf16x8_t a =
+                        *(const bf16x8_t*)(sH + (r * 32 + n) * LDH + (c0 + 4 * j + w) * 8);
+                    acc[i][r] = mfma_32x32x16(a, bw, acc[i][r]);
+                }
             }
     }
 
@@ -619,13 +633,15 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     for (int i = 0; i < TPW; ++i) {
         const int col = (i * WAVES + wave) * 32 + n;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = 8 * (e / 4) + 4 * hf + (e % 4);
-            sO[row * CGS + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][e]);
-        }
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = r * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
+                sO[row * CGS + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][r][e]);
+            }
     }
     __syncthreads();
-    constexpr int OPIECES = 32 * CG / 8;
+    constexpr int OPIECES = MT * CG / 8;
     const int ncols = min(CG, N - n_base);
     for (int qq = tid; qq < OPIECES; qq += NT) {
         const int row = qq / (CG / 8), c8 = (qq % (CG / 8)) * 8;
@@ -635,11 +651,11 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     }
 }
 
-template <int KW, int TPW, int WAVES>
+template <int KW, int TPW, int WAVES, int MT = 32>
 static size_t down_tiles_lds_bytes() {
     constexpr int K = KW * 64, CG = WAVES * TPW * 32;
-    const size_t a = (size_t)32 * (K + 8) * 2 + (size_t)2 * CG * (KW + 2) * 2;
-    const size_t o = (size_t)32 * (CG + 8) * 2;
+    const size_t a = (size_t)MT * (K + 8) * 2 + (size_t)2 * CG * (KW + 2) * 2;
+    const size_t o = (size_t)MT * (CG + 8) * 2;
     return a > o ? a : o;
 }
 
@@ -771,14 +787,40 @@ hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
 #define MOE_DT_TPW 2
 #endif
 
-template <int KW>
-static void launch_down_tiles(GroupedArgs a, int br, int n_max, int slots, hipStream_t stream) {
-    constexpr int cg = MOE_DT_WAVES * MOE_DT_TPW * 32;
+#ifndef MOE_DP_WAVES
+#define MOE_DP_WAVES 8
+#endif
+#ifndef MOE_DP_TPW
+#define MOE_DP_TPW 1
+#endif
+
+template <int KW, int TPW, int WAVES, int MT>
+static void launch_down_tiles_mt(GroupedArgs a, int br, int n_max, int slots, hipStream_t stream) {
+    constexpr int cg = WAVES * TPW * 32;
     a.n_tiles = (n_max + cg - 1) / cg;
     const long long items = (long long)slots * a.n_tiles;
     const int grid = (int)((items + kXcds - 1) / kXcds) * kXcds;
-    down_tiles_kernel<KW, MOE_DT_TPW, MOE_DT_WAVES>
-        <<<grid, MOE_DT_WAVES * 64, down_tiles_lds_bytes<KW, MOE_DT_TPW, MOE_DT_WAVES>(), stream>>>(a, br);
+    down_tiles_kernel<KW, TPW, WAVES, MT>
+        <<<grid, WAVES * 64, down_tiles_lds_bytes<KW, TPW, WAVES, MT>(), stream>>>(a, br);
+}
+
+// 64-row items (pairs of 32-row blocks) when the experts average at least
+// MOE_DP_MIN_ROWS rows: each dequantized weight then feeds up to 64 rows.
+#ifndef MOE_DP_MIN_ROWS
+#define MOE_DP_MIN_ROWS 48
+#endif
+
+template <int KW>
+static void launch_down_tiles(GroupedArgs a, const GemmProblem& p, hipStream_t stream) {
+    const bool pair = p.block_rows == 32 && (long long)p.T * p.k >= (long long)MOE_DP_MIN_ROWS * p.E;
+    if (pair) {
+        a.sh_blocks = p.I_sh ? (p.T + 63) / 64 : 0;
+        launch_down_tiles_mt<KW, MOE_DP_TPW, MOE_DP_WAVES, 64>(a, p.block_rows, p.H,
+                                                              a.sh_blocks + p.max_blocks, stream);
+    } else {
+        launch_down_tiles_mt<KW, MOE_DT_TPW, MOE_DT_WAVES, 32>(a, p.block_rows, p.H,
+                                                              a.sh_blocks + p.max_blocks, stream);
+    }
 }
 
 // The whole-K tile kernel serves row blocks of up to 32 rows with one K
@@ -796,11 +838,10 @@ static bool down_tiles_fits(const GemmProblem& p) {
 hipError_t launch_down(const GemmProblem& p, const void* ws, hipStream_t stream) {
     const GroupedArgs a = down_args(p, ws);
     if (down_tiles_fits(p)) {
-        const int slots = a.sh_blocks + p.max_blocks;
-        if (p.I == 512) launch_down_tiles<8>(a, p.block_rows, p.H, slots, stream);
-        else if (p.I == 256) launch_down_tiles<4>(a, p.block_rows, p.H, slots, stream);
-        else if (p.I == 128) launch_down_tiles<2>(a, p.block_rows, p.H, slots, stream);
-        else launch_down_tiles<1>(a, p.block_rows, p.H, slots, stream);
+        if (p.I == 512) launch_down_tiles<8>(a, p, stream);
+        else if (p.I == 256) launch_down_tiles<4>(a, p, stream);
+        else if (p.I == 128) launch_down_tiles<2>(a, p, stream);
+        else launch_down_tiles<1>(a, p, stream);
         return hipGetLastError();
     }
     launch_grouped<1, MOE_DN_NSUB, MOE_DN_DEPTH, MOE_DN_WAVES>(

@@ -52,6 +52,7 @@ SHAPES = [
     (37, 256, 128, 8, 3, 0, 16),
     (130, 384, 192, 12, 2, 320, 64),      # K = 192 and 320: the 64-K chunk path
     (70, 384, 512, 8, 2, 512, 32),        # down K = 512 over whole-K tiles, partial column group
+    (301, 320, 512, 4, 2, 512, 32),       # 64-row down items (block pairs), partial column group
 ]
 
 
