@@ -82,14 +82,18 @@ def test_layer_outputs_identical_in_both_layouts(T, H, I, E, k, I_sh, block_rows
         assert np.array_equal(ys[0], ys[1]), f"decode token {t}"
 
 
-def test_prefill512_identical_in_both_layouts():
-    cfg = CONFIGS["prefill512"]
+@pytest.mark.parametrize("name", ["prefill512", "prefill2048"])
+def test_prefill_identical_in_both_layouts(name):
+    """The bench times the tile-packed order; the full-size workloads must give
+    the row-major order's outputs bit for bit (2048 tokens also takes the
+    64-row paired down items)."""
+    cfg = CONFIGS[name]
     w = make_weights(cfg, seed=0)
     rows = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
     tiles = bq.MoeLayer.from_device([None if m is None else m.prepacked() for m in rows.weight_mats()],
                                     cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
     x_bits, logits = make_activations(cfg)
-    announce("layouts prefill512")
+    announce(f"layouts {name}")
     a = run_layer(rows, x_bits, logits)
     b = run_layer(tiles, x_bits, logits)
     assert np.array_equal(a["y"], b["y"])
