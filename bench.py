@@ -87,6 +87,23 @@ def only_set(args):
     return set(filter(None, args.only.split(",")))
 
 
+def settle(fn, torch, ms=150.0, max_calls=20000):
+    """Run fn back to back until about `ms` of wall time has passed.  After
+    host-bound phases (the host-synced ablation, graph capture) the GPU clocks
+    are low; a count-based warm-up of a few calls would time the ramp."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_calls:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                break
+    torch.cuda.synchronize()
+
+
 def timed(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -439,7 +456,9 @@ def main():
         if not only or "prefill2048" in only:
             c = CONFIGS["prefill2048"]
             x2, lg2 = prep(c)
+            settle(lambda: layer.forward(x2, lg2), torch)
             ms2 = timed(lambda: layer.forward(x2, lg2), max(10, args.steps // 4), 5, torch)
+            settle(cold(lambda L: L.forward(x2, lg2)), torch)
             ms2c = timed(cold(lambda L: L.forward(x2, lg2)), max(10, args.steps // 4), 5, torch)
             cnt = layer.buffers(c.T)["routing"].counts.cpu().numpy()
             tch = int(np.count_nonzero(cnt))
@@ -462,9 +481,10 @@ def main():
             wsd = torch.empty(bq.decode_workspace_bytes(c.H, c.I, c.I_sh, c.E, c.k),
                               dtype=torch.uint8, device=dev)
             # 1000 single-token launches enqueued back to back from C, one per token
-            msd = timed(lambda: bq.moe_decode_q4_sequential(xd, lgd, c.I, c.I_sh, c.k,
-                                                            *layer.weight_mats(), yd, wsd),
-                        3, 1, torch)
+            seq = lambda: bq.moe_decode_q4_sequential(xd, lgd, c.I, c.I_sh, c.k,
+                                                      *layer.weight_mats(), yd, wsd)
+            settle(seq, torch)
+            msd = timed(seq, 3, 1, torch)
             t_tok = msd * 1e-3 / c.T
             by_tok = 9 * expert_bytes + c.H * 4 + c.E * 4
             # the three-call path at T = 1 over the first 100 tokens, for comparison
@@ -499,6 +519,7 @@ def main():
                 graph.replay()
                 torch.cuda.synchronize()
                 graph_ok &= bool(torch.equal(y_graph.view(torch.int16), y_eager.view(torch.int16)))
+            settle(graph.replay, torch)
             t_cold = timed(graph.replay, 3, 1, torch) * 1e-3 / c.T
             del graph
             extra["decode"] = {"tokens_per_s": 1.0 / t_tok, "us_per_token": t_tok * 1e6,
@@ -520,6 +541,7 @@ def main():
             xs_, lgs_ = prep(c)
             y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
             ws = layer.forward_chunked(xs_, lgs_, c.chunk, y)
+            settle(lambda: layer.forward_chunked(xs_, lgs_, c.chunk, y, ws), torch)
             mss = timed(lambda: layer.forward_chunked(xs_, lgs_, c.chunk, y, ws), 10, 2, torch)
             t = mss * 1e-3
             fl = layer_flops(c.T, c.H, c.I, c.k, c.I_sh)
