@@ -29,9 +29,12 @@ int check_layer_shape(int T, int H, int I, int I_sh, int E, int k, int block_row
     const int st = check_route_shape(T, E, k, block_rows);
     if (st) return st;
     if (H < 64 || H % 64 || I < 64 || I % 64 || I_sh < 0 || I_sh % 64) return MOE_ERR_SHAPE;
+    // the kernels form 32-bit byte offsets inside one buffer: bf16 rows of x, h,
+    // expert_out and shared_out, and one expert's code words
     const long long widest = H > I ? H : I;
-    if ((long long)T * k * widest >= (1ll << 31)) return MOE_ERR_SHAPE;
-    if ((long long)T * (I_sh > H ? I_sh : H) >= (1ll << 31)) return MOE_ERR_SHAPE;
+    if ((long long)T * k * widest >= (1ll << 30)) return MOE_ERR_SHAPE;
+    if ((long long)T * (I_sh > H ? I_sh : H) >= (1ll << 30)) return MOE_ERR_SHAPE;
+    if ((long long)H * (I > I_sh ? I : I_sh) >= (1ll << 32)) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -390,6 +393,8 @@ int moe_expert_gateup_bf16(const uint16_t* x, int T, int H, int I, int I_sh, int
     try {
         int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
         if (st) return st;
+        // one expert's bf16 matrix (4x its code bytes) also stays below 2^31 bytes
+        if ((long long)H * (I > I_sh ? I : I_sh) >= (1ll << 30)) return MOE_ERR_SHAPE;
         if (!x) return MOE_ERR_NULL;
         if ((st = check_routing(r))) return st;
         if ((st = check_bf16_weights(gate)) || (st = check_bf16_weights(up))) return st;
@@ -417,6 +422,8 @@ int moe_expert_down_bf16(int T, int H, int I, int I_sh, int E, int k, int block_
     try {
         int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
         if (st) return st;
+        // one expert's bf16 matrix (4x its code bytes) also stays below 2^31 bytes
+        if ((long long)H * (I > I_sh ? I : I_sh) >= (1ll << 30)) return MOE_ERR_SHAPE;
         if (!expert_out) return MOE_ERR_NULL;
         if ((st = check_routing(r))) return st;
         if ((st = check_bf16_weights(down))) return st;
@@ -443,7 +450,7 @@ int moe_combine(const uint16_t* expert_out, const uint16_t* shared_out, const mo
                 int T, int H, int k, uint16_t* y, hipStream_t stream) {
     try {
         if (T < 1 || k < 1 || H < 64 || H % 64) return MOE_ERR_SHAPE;
-        if ((long long)T * k * H >= (1ll << 31)) return MOE_ERR_SHAPE;
+        if ((long long)T * k * H >= (1ll << 30)) return MOE_ERR_SHAPE;
         if (!expert_out || !y || !r || !r->assign_row || !r->topk_w) return MOE_ERR_NULL;
         if (!aligned(expert_out, 16) || !aligned(y, 16) || (shared_out && !aligned(shared_out, 16)))
             return MOE_ERR_ALIGN;
@@ -460,7 +467,7 @@ int moe_combine_gated(const uint16_t* expert_out, const uint16_t* shared_out,
                       uint16_t* y, hipStream_t stream) {
     try {
         if (T < 1 || k < 1 || H < 64 || H % 64) return MOE_ERR_SHAPE;
-        if ((long long)T * k * H >= (1ll << 31)) return MOE_ERR_SHAPE;
+        if ((long long)T * k * H >= (1ll << 30)) return MOE_ERR_SHAPE;
         if (!expert_out || !shared_out || !shared_gate || !y || !r || !r->assign_row || !r->topk_w)
             return MOE_ERR_NULL;
         if (!aligned(expert_out, 16) || !aligned(y, 16) || !aligned(shared_out, 16) ||

@@ -31,7 +31,9 @@
  *   - The library holds no mutable global state: calls on different streams
  *     may run concurrently from different threads if their buffers differ.
  *   - Shapes: 1 <= k <= E <= 1000; H, I, I_sh are multiples of 64 (I_sh = 0
- *     means no shared expert); T >= 1; T*k*max(H, I) < 2^31;
+ *     means no shared expert); T >= 1; T*k*max(H, I) < 2^30 and
+ *     T*max(H, I_sh) < 2^30 (bf16 byte offsets of x, h and the outputs fit
+ *     in 31 bits); H*max(I, I_sh) < 2^32 (one expert's code words);
  *     block_rows is 16, 32 or 64.
  *   - Inputs are finite.  Scales must satisfy |s| < 2^118 (the kernels work
  *     with 512*s internally).
@@ -210,7 +212,9 @@ int moe_dequant_q4_bf16(const moe_q4_mat* m, int n_exp, int N, int K, const int3
  * bf16 (e.g. by moe_dequant_q4_bf16): gate/up bf16 [E, I, H], shared [1, I_sh, H],
  * down bf16 [E, H, I], shared [1, H, I_sh], each 16-byte aligned.  Same
  * routing, workspace and outputs as the 4-bit entry points; the GEMM tiles
- * and pipeline are the same, only the weight operand is read as bf16. */
+ * and pipeline are the same, only the weight operand is read as bf16.
+ * Shapes as for the 4-bit calls, and H*max(I, I_sh) < 2^30 (one expert's
+ * bf16 matrix below 2^31 bytes). */
 int moe_expert_gateup_bf16(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
                            int block_rows, const moe_routing* r, const uint16_t* gate,
                            const uint16_t* up, const uint16_t* sh_gate, const uint16_t* sh_up,

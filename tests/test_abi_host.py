@@ -49,6 +49,28 @@ def test_max_blocks_and_workspace_sizes():
     assert bq.layer_workspace_bytes(2048, 2048, 512, 512, 256, 8, 32) > 2048 * 8 * 2048 * 2
 
 
+def test_shape_limits_keep_byte_offsets_in_31_bits():
+    """The kernels form 32-bit byte offsets inside one buffer: T*k*max(H, I) and
+    T*max(H, I_sh) bf16 elements stay below 2^30, one expert's H*max(I, I_sh) / 2
+    bytes of code words below 2^31."""
+    ws = bq.gemm_workspace_bytes
+    # T*k*H = 2^30 - 2^21 (accepted) and 2^30 (rejected), H = 2048, k = 8
+    assert ws(65536 - 128, 2048, 512, 512, 256, 8, 32) > 0
+    assert ws(65536, 2048, 512, 512, 256, 8, 32) == 0
+    # T*I_sh = 2^30 with k = 1, H = 64 (T*k*max(H, I) stays below the bound)
+    assert ws(1 << 14, 64, 64, 1 << 16, 256, 1, 32) == 0
+    assert ws((1 << 14) - 1, 64, 64, 1 << 16, 256, 1, 32) > 0
+    # H*I = 2^32 (one expert's codes would be 2^31 bytes) with T = 1
+    assert ws(1, 65536, 65536, 0, 4, 1, 32) == 0
+    assert ws(1, 65536, 65536 - 64, 0, 4, 1, 32) > 0
+    L = bq.lib()
+    r = _routing()
+    assert L.moe_combine(FAKE, None, ctypes.byref(r), 65536, 2048, 8, FAKE, None) == bq.MOE_ERR_SHAPE
+    # the bf16-weight GEMMs: one expert's bf16 matrix below 2^31 bytes (H*I < 2^30)
+    args = lambda H, I: [1, H, I, 0, 4, 1, 32, ctypes.byref(r), FAKE, None, FAKE, None, FAKE, 1 << 40, None]  # noqa: E731
+    assert L.moe_expert_down_bf16(*args(32768, 32768)) == bq.MOE_ERR_SHAPE
+
+
 P = ctypes.c_void_p
 FAKE = P(0x10000)          # never dereferenced: validation fails first
 MISALIGNED = P(0x10008)
