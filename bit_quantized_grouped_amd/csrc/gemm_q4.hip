@@ -447,11 +447,13 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
 }
 
 // ---- Down projection over whole-K tiles (K = I <= 512) ----
-// Work item = one row block (<= 32 rows) x CG = WAVES * TPW * 32 output
-// columns.  The block's h rows (32 x K bf16) are staged in LDS once per item
-// and every wave reads them; each wave owns TPW tiles of 32 output columns
-// over the whole K and requests all of their code words before staging h,
-// so the item streams its weights in one round of loads.  The product is
+// Work item = one row block (MT = 32 rows, or 64 from two blocks, below) x
+// CG = WAVES * TPW * 32 output columns.  The block's h rows (MT x K bf16) are
+// staged in LDS once per item and every wave reads them; each wave owns TPW
+// tiles of 32 output columns over the whole K and requests all of their code
+// words right after the h rows and scales, so the item streams its weights in
+// one round of loads and the math on tile 0 starts while tile 1's words are
+// still arriving.  The product is
 // v_mfma_f32_32x32x16_bf16: lane half hf (lane / 32) takes the words of the
 // second half of K when hf = 1, so each lane reads half a weight row (K / 4
 // bytes) contiguously and its A elements come from the same K positions.
