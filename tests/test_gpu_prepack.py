@@ -98,3 +98,14 @@ def test_prefill_identical_in_both_layouts(name):
     b = run_layer(tiles, x_bits, logits)
     assert np.array_equal(a["y"], b["y"])
     assert np.array_equal(a["expert_out"], b["expert_out"])
+    # batch-1 decode over the same full-size weights, as the bench times it
+    for t in (0, cfg.T // 2, cfg.T - 1):
+        ys = []
+        for L in (rows, tiles):
+            xt = bq.bf16_from_bits(x_bits[t:t + 1], DEV)
+            lg = torch.from_numpy(np.ascontiguousarray(logits[t:t + 1])).to(DEV)
+            y = torch.empty((1, cfg.H), dtype=torch.bfloat16, device=DEV)
+            L.decode(xt, lg, y)
+            torch.cuda.synchronize()
+            ys.append(bq.bf16_to_bits(y))
+        assert np.array_equal(ys[0], ys[1]), f"decode token {t}"
