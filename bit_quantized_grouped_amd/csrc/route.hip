@@ -116,6 +116,48 @@ __device__ void block_exclusive_scan2(int a, int b, int* s_wave, int* ex_a, int*
     __syncthreads();
 }
 
+// Per expert: prefix of the kGroupWaves segment counts in s_hist, totals
+// (counts), exclusive scan (offsets), the block map and n_blocks; afterwards
+// s_hist[w * E + e] holds the first row of segment w's assignments to e.
+__device__ void group_scan_block_map(int E, int block_rows, int max_blocks, const RoutingDev& r,
+                                     int* s_hist) {
+    const int tid = threadIdx.x;
+    int* s_wave = s_hist + kGroupWaves * E;
+    const int e = tid;
+    int h[kGroupWaves];
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) h[w] = e < E ? s_hist[w * E + e] : 0;
+    int cnt = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) cnt += h[w];
+    const int nb = e < E ? (cnt + block_rows - 1) / block_rows : 0;
+    int off, bstart, total_rows, total_blocks;
+    block_exclusive_scan2(cnt, nb, s_wave, &off, &bstart, &total_rows, &total_blocks);
+    if (e < E) {
+        r.counts[e] = cnt;
+        r.offsets[e] = off;
+        for (int i = 0; i < nb; ++i) {
+            r.block_expert[bstart + i] = e;
+            r.block_row[bstart + i] = off + block_rows * i;
+        }
+        int run = off;
+#pragma unroll
+        for (int w = 0; w < kGroupWaves; ++w) {
+            s_hist[w * E + e] = run;
+            run += h[w];
+        }
+    }
+    if (e == 0) {
+        r.offsets[E] = total_rows;
+        r.n_blocks[0] = total_blocks;
+    }
+    for (int b = total_blocks + tid; b < max_blocks; b += kGroupThreads) {
+        r.block_expert[b] = -1;
+        r.block_row[b] = -1;
+    }
+    __syncthreads();
+}
+
 // Histogram, scan, block map and stable scatter of n = T*k assignments
 // whose experts are eids[0..n).  Needs kGroupThreads threads and
 // kGroupWaves*E + 2*(kGroupWaves+1) ints of LDS at s_hist.
@@ -135,7 +177,6 @@ __device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int
                           const RoutingDev& r, int* s_hist) {
     constexpr int kPre = 16;
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    int* s_wave = s_hist + kGroupWaves * E;
     const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
     const int seg = (n + kGroupWaves - 1) / kGroupWaves;
     const int a_begin = min(n, wave * seg), a_end = min(n, a_begin + seg);
@@ -197,41 +238,7 @@ __device__ void group_all(const int32_t* eids, int n, int E, int block_rows, int
     }
     __syncthreads();
 
-    // per expert: prefix over segments, totals, scans, block map
-    const int e = tid;
-    int h[kGroupWaves];
-#pragma unroll
-    for (int w = 0; w < kGroupWaves; ++w) h[w] = e < E ? s_hist[w * E + e] : 0;
-    int cnt = 0;
-#pragma unroll
-    for (int w = 0; w < kGroupWaves; ++w) cnt += h[w];
-    const int nb = e < E ? (cnt + block_rows - 1) / block_rows : 0;
-    int off, bstart, total_rows, total_blocks;
-    block_exclusive_scan2(cnt, nb, s_wave, &off, &bstart, &total_rows, &total_blocks);
-    if (e < E) {
-        r.counts[e] = cnt;
-        r.offsets[e] = off;
-        for (int i = 0; i < nb; ++i) {
-            r.block_expert[bstart + i] = e;
-            r.block_row[bstart + i] = off + block_rows * i;
-        }
-        int run = off;
-#pragma unroll
-        for (int w = 0; w < kGroupWaves; ++w) {
-            s_hist[w * E + e] = run;
-            run += h[w];
-        }
-    }
-    if (e == 0) {
-        r.offsets[E] = total_rows;
-        r.n_blocks[0] = total_blocks;
-    }
-    for (int b = total_blocks + tid; b < max_blocks; b += kGroupThreads) {
-        r.block_expert[b] = -1;
-        r.block_row[b] = -1;
-    }
-    __syncthreads();
-
+    group_scan_block_map(E, block_rows, max_blocks, r, s_hist);
     // pass 2: stable scatter
     if (one_batch) {
         scatter(a_begin, ids, mm);
@@ -255,6 +262,129 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
     group_all(topk_idx, n, E, block_rows, max_blocks, r, smem_i);
 }
 
+// k = 8 with T above the one-launch size: the top-k kernel takes 8 tokens per
+// workgroup, i.e. one 64-assignment chunk, and records each assignment's
+// match information inside that chunk (the lane of the first equal expert,
+// the rank among equal experts in lower lanes, the group size), so the
+// one-workgroup grouping pass needs no ballots.  The chunks are those of
+// group_all_info below: chunk c = assignments [64c, 64c + 64).
+constexpr int kChunkK = 8;
+constexpr int kChunkTokens = WAVE / kChunkK;
+
+__device__ __forceinline__ uint32_t chunk_info(uint64_t match) {
+    const uint32_t leader = (uint32_t)__builtin_ctzll(match);
+    const uint32_t rank = (uint32_t)__popcll(match & lanemask_lt());
+    const uint32_t size = (uint32_t)__popcll(match);
+    return leader | (rank << 8) | (size << 16);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kChunkTokens * WAVE) void route_topk_chunk_kernel(
+    const float* __restrict__ logits, int T, int E, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, uint32_t* __restrict__ info) {
+    __shared__ uint32_t s_scr[kChunkTokens][3 * kChunkK];
+    __shared__ int s_chunk[WAVE];
+    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+    const int t = blockIdx.x * kChunkTokens + wave;
+    if (t < T)
+        topk_token<EPL>(logits + (size_t)t * E, E, kChunkK, topk_idx + (size_t)t * kChunkK,
+                        topk_w + (size_t)t * kChunkK, s_scr[wave], (int*)(s_scr[wave] + kChunkK),
+                        (float*)(s_scr[wave] + 2 * kChunkK), s_chunk + wave * kChunkK);
+    __syncthreads();
+    if (wave == 0) {
+        const int a = blockIdx.x * WAVE + lane;
+        const bool valid = a < T * kChunkK;
+        const int e = valid ? s_chunk[lane] : 0;
+        const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
+        const uint64_t m = match_mask(e, valid, nbits);
+        if (valid) info[a] = chunk_info(m);
+    }
+}
+
+// group_all with the chunk match information precomputed: wave w owns the
+// contiguous chunks w*seg .. of the assignments.  Pass 1: chunk leaders add
+// their group's size to the wave's histogram.  Pass 2: leaders take their
+// group's first row with a returning LDS add on the running per-expert row and
+// hand it to the group; a lane's row is that plus its rank.  The rows are the
+// same stable counting sort as group_all's.
+__device__ void group_all_info(const int32_t* eids, const uint32_t* info, int n, int E,
+                               int block_rows, int max_blocks, const RoutingDev& r, int* s_hist) {
+    constexpr int kPre = 16;
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int n_chunks = (n + WAVE - 1) / WAVE;
+    const int seg = (n_chunks + kGroupWaves - 1) / kGroupWaves;
+    const int c_begin = min(n_chunks, wave * seg), c_end = min(n_chunks, c_begin + seg);
+    int* my_hist = s_hist + wave * E;
+
+    for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) s_hist[i] = 0;
+    __syncthreads();
+
+    auto load = [&](int cb, int (&ids)[kPre], uint32_t (&inf)[kPre]) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int a = (cb + q) * WAVE + lane;
+            const bool ok = cb + q < c_end && a < n;
+            ids[q] = ok ? eids[a] : 0;
+            inf[q] = ok ? info[a] : 0u;
+        }
+    };
+    auto count = [&](int cb, const int (&ids)[kPre], const uint32_t (&inf)[kPre]) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            if (cb + q >= c_end) break;
+            const int a = (cb + q) * WAVE + lane;
+            if (a < n && (int)(inf[q] & 0xFFu) == lane) atomicAdd(&my_hist[ids[q]], (int)(inf[q] >> 16));
+        }
+    };
+    auto scatter = [&](int cb, const int (&ids)[kPre], const uint32_t (&inf)[kPre]) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            if (cb + q >= c_end) break;
+            const int a = (cb + q) * WAVE + lane;
+            const bool valid = a < n;
+            const int leader = valid ? (int)(inf[q] & 0xFFu) : lane;
+            int first = 0;
+            if (valid && leader == lane) first = atomicAdd(&my_hist[ids[q]], (int)(inf[q] >> 16));
+            first = __shfl(first, leader, WAVE);
+            if (valid) {
+                const int row = first + (int)((inf[q] >> 8) & 0xFFu);
+                r.sorted_assign[row] = a;
+                r.assign_row[a] = row;
+            }
+        }
+    };
+
+    const bool one_batch = c_end - c_begin <= kPre;   // uniform per wave
+    int ids[kPre];
+    uint32_t inf[kPre];
+    if (one_batch) {
+        load(c_begin, ids, inf);
+        count(c_begin, ids, inf);
+    } else {
+        for (int cb = c_begin; cb < c_end; cb += kPre) {
+            load(cb, ids, inf);
+            count(cb, ids, inf);
+        }
+    }
+    __syncthreads();
+    group_scan_block_map(E, block_rows, max_blocks, r, s_hist);
+    if (one_batch) {
+        scatter(c_begin, ids, inf);
+    } else {
+        for (int cb = c_begin; cb < c_end; cb += kPre) {
+            load(cb, ids, inf);
+            scatter(cb, ids, inf);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void route_group_info_kernel(
+    const int32_t* __restrict__ topk_idx, const uint32_t* __restrict__ info, int n, int E,
+    int block_rows, int max_blocks, RoutingDev r) {
+    extern __shared__ int smem_i[];
+    group_all_info(topk_idx, info, n, E, block_rows, max_blocks, r, smem_i);
+}
+
 // Small T: every wave takes tokens wave, wave+16, ...; experts are kept in
 // LDS for the grouping phase, so the whole routing is one launch.
 template <int EPL>
@@ -275,15 +405,6 @@ __global__ __launch_bounds__(kGroupThreads) void route_fused_kernel(
     group_all(s_eids, T * k, E, block_rows, max_blocks, r, s_hist);
 }
 
-size_t route_ws_layout(int T, int E, int k, size_t* off_hist, size_t* off_rank) {
-    (void)T;
-    (void)E;
-    (void)k;
-    *off_hist = 0;
-    *off_rank = 0;
-    return 0;   // routing needs no device workspace beyond its outputs
-}
-
 static size_t group_lds_bytes(int E) {
     return (size_t)(kGroupWaves * E + 2 * (kGroupWaves + 1)) * sizeof(int);
 }
@@ -295,12 +416,29 @@ static size_t fused_lds_bytes(int T, int E, int k) {
 
 constexpr size_t kMaxLds = 64 * 1024;
 
+static bool use_fused(int T, int E, int k) {
+    return T <= kFusedMaxTokens && fused_lds_bytes(T, E, k) <= kMaxLds;
+}
+
+// k = 8 outside the one-launch path: the top-k kernel records per-chunk match
+// information for the grouping pass (T * k words of workspace).
+static bool use_chunk_info(int T, int E, int k) {
+    return k == kChunkK && !use_fused(T, E, k);
+}
+
+size_t route_ws_layout(int T, int E, int k, size_t* off_hist, size_t* off_rank) {
+    *off_hist = 0;
+    *off_rank = 0;
+    if (!use_chunk_info(T, E, k)) return 0;   // no device workspace beyond the outputs
+    return align_up((size_t)T * k * sizeof(uint32_t), 256);
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int block_rows, int max_blocks,
                         const RoutingDev& r, void* ws, hipStream_t stream) {
     (void)ws;
     const int epl = (E + WAVE - 1) / WAVE;
     const int n = T * k;
-    if (T <= kFusedMaxTokens && fused_lds_bytes(T, E, k) <= kMaxLds) {
+    if (use_fused(T, E, k)) {
         const size_t smem = fused_lds_bytes(T, E, k);
 #define MOE_FUSED(N)                                                                          \
     route_fused_kernel<N><<<1, kGroupThreads, smem, stream>>>(logits, T, E, k, block_rows,     \
@@ -311,6 +449,22 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int block_rows
         else if (epl <= 8) MOE_FUSED(8);
         else MOE_FUSED(16);
 #undef MOE_FUSED
+        return hipGetLastError();
+    }
+    if (use_chunk_info(T, E, k)) {
+        uint32_t* info = (uint32_t*)ws;
+        const int grid_c = (T + kChunkTokens - 1) / kChunkTokens;
+#define MOE_TOPK_CHUNK(N)                                                                    \
+    route_topk_chunk_kernel<N><<<grid_c, kChunkTokens * WAVE, 0, stream>>>(logits, T, E,    \
+                                                                           r.topk_idx, r.topk_w, info)
+        if (epl <= 1) MOE_TOPK_CHUNK(1);
+        else if (epl <= 2) MOE_TOPK_CHUNK(2);
+        else if (epl <= 4) MOE_TOPK_CHUNK(4);
+        else if (epl <= 8) MOE_TOPK_CHUNK(8);
+        else MOE_TOPK_CHUNK(16);
+#undef MOE_TOPK_CHUNK
+        route_group_info_kernel<<<1, kGroupThreads, group_lds_bytes(E), stream>>>(
+            r.topk_idx, info, n, E, block_rows, max_blocks, r);
         return hipGetLastError();
     }
     const size_t smem_t = (size_t)kTopkWaves * 3 * k * sizeof(uint32_t);
