@@ -65,22 +65,30 @@ __device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
     return match;
 }
 
+// Inclusive sum over the wave's lanes.  DPP row_shr 1, 2, 4, 8 scan each
+// 16-lane row; row_bcast 15 then adds row 0's total into row 1 (and row 2's
+// into row 3), row_bcast 31 the first two rows' total into rows 2 and 3.
+// Lanes without a source (or in rows the mask leaves out) add 0.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+#define MOE_DPP_ADD(ctrl, rows) v += __builtin_amdgcn_update_dpp(0, v, ctrl, rows, 0xf, false)
+    MOE_DPP_ADD(0x111, 0xf);   // row_shr:1
+    MOE_DPP_ADD(0x112, 0xf);   // row_shr:2
+    MOE_DPP_ADD(0x114, 0xf);   // row_shr:4
+    MOE_DPP_ADD(0x118, 0xf);   // row_shr:8
+    MOE_DPP_ADD(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    MOE_DPP_ADD(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef MOE_DPP_ADD
+    return v;
+}
+
 // Exclusive scan of two values per thread over a kGroupThreads workgroup
 // (s_wave: 2 * (kGroupWaves + 1) ints).  Returns the scans of a and b and
 // both totals.
 __device__ void block_exclusive_scan2(int a, int b, int* s_wave, int* ex_a, int* ex_b,
                                       int* tot_a, int* tot_b) {
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    int ia = a, ib = b;
-#pragma unroll
-    for (int off = 1; off < WAVE; off <<= 1) {
-        const int oa = __shfl_up(ia, off, WAVE);
-        const int ob = __shfl_up(ib, off, WAVE);
-        if (lane >= off) {
-            ia += oa;
-            ib += ob;
-        }
-    }
+    const int ia = wave_incl_sum(a);
+    const int ib = wave_incl_sum(b);
     if (lane == WAVE - 1) {
         s_wave[wave] = ia;
         s_wave[kGroupWaves + 1 + wave] = ib;
@@ -89,16 +97,8 @@ __device__ void block_exclusive_scan2(int a, int b, int* s_wave, int* ex_a, int*
     if (wave == 0) {
         const int wa = lane < kGroupWaves ? s_wave[lane] : 0;
         const int wb = lane < kGroupWaves ? s_wave[kGroupWaves + 1 + lane] : 0;
-        int xa = wa, xb = wb;
-#pragma unroll
-        for (int off = 1; off < kGroupWaves; off <<= 1) {
-            const int oa = __shfl_up(xa, off, WAVE);
-            const int ob = __shfl_up(xb, off, WAVE);
-            if (lane >= off) {
-                xa += oa;
-                xb += ob;
-            }
-        }
+        const int xa = wave_incl_sum(wa);
+        const int xb = wave_incl_sum(wb);
         if (lane < kGroupWaves) {
             s_wave[lane] = xa - wa;
             s_wave[kGroupWaves + 1 + lane] = xb - wb;
@@ -316,9 +316,6 @@ __device__ void group_all_info(const int32_t* eids, const uint32_t* info, int n,
     const int c_begin = min(n_chunks, wave * seg), c_end = min(n_chunks, c_begin + seg);
     int* my_hist = s_hist + wave * E;
 
-    for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) s_hist[i] = 0;
-    __syncthreads();
-
     auto load = [&](int cb, int (&ids)[kPre], uint32_t (&inf)[kPre]) {
 #pragma unroll
         for (int q = 0; q < kPre; ++q) {
@@ -357,8 +354,12 @@ __device__ void group_all_info(const int32_t* eids, const uint32_t* info, int n,
     const bool one_batch = c_end - c_begin <= kPre;   // uniform per wave
     int ids[kPre];
     uint32_t inf[kPre];
+    if (one_batch) load(c_begin, ids, inf);
+    // Each wave clears only its own histogram, while its loads are in flight;
+    // a wave's LDS operations execute in program order, so its adds below
+    // follow the clear without a barrier.
+    for (int i = lane; i < E; i += WAVE) my_hist[i] = 0;
     if (one_batch) {
-        load(c_begin, ids, inf);
         count(c_begin, ids, inf);
     } else {
         for (int cb = c_begin; cb < c_end; cb += kPre) {
