@@ -3,6 +3,7 @@
 import numpy as np
 import pytest
 
+import bit_quantized_grouped_amd as bq
 from gpu_cases import announce, assert_routing_matches, gpu_route, require_gpu
 from workload import CONFIGS, make_activations
 
@@ -67,6 +68,24 @@ def test_route_ties(T, E, k, levels, seed):
     L = _tie_heavy(T, E, levels, seed)
     announce(f"route ties T={T} E={E} k={k}")
     assert_routing_matches(gpu_route(L, k, 32), L, k, 32)
+
+
+@pytest.mark.parametrize("T,E,levels,br,seed", [
+    (65, 256, 3, 32, 11),      # one token in the last 8-token chunk
+    (72, 8, 1, 32, 12),        # E = k = 8: every expert 8 times in every chunk
+    (129, 1000, 4, 16, 13),    # E up to 1000
+    (1000, 256, 2, 64, 14),    # heavy ties, 64-row blocks
+    (3000, 256, 5, 32, 15),    # more than 16 chunks per grouping wave: batched reloads
+    (4097, 64, 3, 16, 16),     # ragged tail over many batches
+])
+def test_route_chunk_match_path(T, E, levels, br, seed):
+    """k = 8 above 64 tokens: the top-k pass records each 64-assignment chunk's
+    match information and the grouping pass uses it (route workspace of T*k
+    words); the routing arrays must still match the oracle bit for bit."""
+    assert bq.route_workspace_bytes(T, E, 8, br) >= T * 8 * 4
+    L = _tie_heavy(T, E, levels, seed)
+    announce(f"route chunk path T={T} E={E} levels={levels} br={br}")
+    assert_routing_matches(gpu_route(L, 8, br), L, 8, br)
 
 
 def test_route_all_equal_and_signed_zero():
