@@ -11,7 +11,7 @@ using namespace moeq4;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kMaxE = 1000;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }

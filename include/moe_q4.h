@@ -109,7 +109,9 @@ typedef struct {
     int32_t* n_blocks;
 } moe_routing;
 
-/* Version of this ABI (bumped on any signature change). */
+/* Version of this ABI (bumped on any change of a signature or of a call's
+ * requirements, such as the workspace it needs; 4: moe_route takes a
+ * workspace for k = 8 above 64 tokens). */
 int moe_abi_version(void);
 
 /* Human-readable text of a status code (static string; never NULL). */

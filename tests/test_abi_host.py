@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert bq.abi_version() == 3
+    assert bq.abi_version() == 4
     for st, txt in [(0, "ok"), (-1, "null pointer"), (-2, "bad shape"), (-3, "misaligned pointer"),
                     (-4, "workspace too small"), (-5, "HIP launch error"), (-6, "unimplemented"),
                     (-99, "unknown status")]:
