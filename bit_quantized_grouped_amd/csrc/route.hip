@@ -262,14 +262,12 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
     group_all(topk_idx, n, E, block_rows, max_blocks, r, smem_i);
 }
 
-// k = 8 with T above the one-launch size: the top-k kernel takes 8 tokens per
-// workgroup, i.e. one 64-assignment chunk, and records each assignment's
-// match information inside that chunk (the lane of the first equal expert,
-// the rank among equal experts in lower lanes, the group size), so the
-// one-workgroup grouping pass needs no ballots.  The chunks are those of
-// group_all_info below: chunk c = assignments [64c, 64c + 64).
-constexpr int kChunkK = 8;
-constexpr int kChunkTokens = WAVE / kChunkK;
+// k = 4, 8 or 16 with T above the one-launch size: the top-k kernel takes
+// 64 / k tokens per workgroup, i.e. one 64-assignment chunk, and records each
+// assignment's match information inside that chunk (the lane of the first
+// equal expert, the rank among equal experts in lower lanes, the group size),
+// so the one-workgroup grouping pass needs no ballots.  The chunks are those
+// of group_all_info below: chunk c = assignments [64c, 64c + 64).
 
 __device__ __forceinline__ uint32_t chunk_info(uint64_t match) {
     const uint32_t leader = (uint32_t)__builtin_ctzll(match);
@@ -278,22 +276,23 @@ __device__ __forceinline__ uint32_t chunk_info(uint64_t match) {
     return leader | (rank << 8) | (size << 16);
 }
 
-template <int EPL>
-__global__ __launch_bounds__(kChunkTokens * WAVE) void route_topk_chunk_kernel(
+template <int EPL, int KK>
+__global__ __launch_bounds__((WAVE / KK) * WAVE) void route_topk_chunk_kernel(
     const float* __restrict__ logits, int T, int E, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, uint32_t* __restrict__ info) {
-    __shared__ uint32_t s_scr[kChunkTokens][3 * kChunkK];
+    constexpr int TOK = WAVE / KK;   // tokens per workgroup: one 64-assignment chunk
+    __shared__ uint32_t s_scr[TOK][3 * KK];
     __shared__ int s_chunk[WAVE];
     const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-    const int t = blockIdx.x * kChunkTokens + wave;
+    const int t = blockIdx.x * TOK + wave;
     if (t < T)
-        topk_token<EPL>(logits + (size_t)t * E, E, kChunkK, topk_idx + (size_t)t * kChunkK,
-                        topk_w + (size_t)t * kChunkK, s_scr[wave], (int*)(s_scr[wave] + kChunkK),
-                        (float*)(s_scr[wave] + 2 * kChunkK), s_chunk + wave * kChunkK);
+        topk_token<EPL>(logits + (size_t)t * E, E, KK, topk_idx + (size_t)t * KK,
+                        topk_w + (size_t)t * KK, s_scr[wave], (int*)(s_scr[wave] + KK),
+                        (float*)(s_scr[wave] + 2 * KK), s_chunk + wave * KK);
     __syncthreads();
     if (wave == 0) {
         const int a = blockIdx.x * WAVE + lane;
-        const bool valid = a < T * kChunkK;
+        const bool valid = a < T * KK;
         const int e = valid ? s_chunk[lane] : 0;
         const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
         const uint64_t m = match_mask(e, valid, nbits);
@@ -421,10 +420,11 @@ static bool use_fused(int T, int E, int k) {
     return T <= kFusedMaxTokens && fused_lds_bytes(T, E, k) <= kMaxLds;
 }
 
-// k = 8 outside the one-launch path: the top-k kernel records per-chunk match
+// k = 4, 8 or 16 outside the one-launch path (64 / k tokens per top-k
+// workgroup, at most 16 waves): the top-k kernel records per-chunk match
 // information for the grouping pass (T * k words of workspace).
 static bool use_chunk_info(int T, int E, int k) {
-    return k == kChunkK && !use_fused(T, E, k);
+    return (k == 4 || k == 8 || k == 16) && !use_fused(T, E, k);
 }
 
 size_t route_ws_layout(int T, int E, int k, size_t* off_hist, size_t* off_rank) {
@@ -454,15 +454,21 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int block_rows
     }
     if (use_chunk_info(T, E, k)) {
         uint32_t* info = (uint32_t*)ws;
-        const int grid_c = (T + kChunkTokens - 1) / kChunkTokens;
-#define MOE_TOPK_CHUNK(N)                                                                    \
-    route_topk_chunk_kernel<N><<<grid_c, kChunkTokens * WAVE, 0, stream>>>(logits, T, E,    \
-                                                                           r.topk_idx, r.topk_w, info)
-        if (epl <= 1) MOE_TOPK_CHUNK(1);
-        else if (epl <= 2) MOE_TOPK_CHUNK(2);
-        else if (epl <= 4) MOE_TOPK_CHUNK(4);
-        else if (epl <= 8) MOE_TOPK_CHUNK(8);
-        else MOE_TOPK_CHUNK(16);
+        const int tok = WAVE / k;
+        const int grid_c = (T + tok - 1) / tok;
+#define MOE_TOPK_CHUNK(N, KK)                                                                 \
+    route_topk_chunk_kernel<N, KK><<<grid_c, tok * WAVE, 0, stream>>>(logits, T, E, r.topk_idx, \
+                                                                       r.topk_w, info)
+#define MOE_TOPK_CHUNK_K(KK)                          \
+        if (epl <= 1) MOE_TOPK_CHUNK(1, KK);          \
+        else if (epl <= 2) MOE_TOPK_CHUNK(2, KK);     \
+        else if (epl <= 4) MOE_TOPK_CHUNK(4, KK);     \
+        else if (epl <= 8) MOE_TOPK_CHUNK(8, KK);     \
+        else MOE_TOPK_CHUNK(16, KK);
+        if (k == 4) { MOE_TOPK_CHUNK_K(4) }
+        else if (k == 8) { MOE_TOPK_CHUNK_K(8) }
+        else { MOE_TOPK_CHUNK_K(16) }
+#undef MOE_TOPK_CHUNK_K
 #undef MOE_TOPK_CHUNK
         route_group_info_kernel<<<1, kGroupThreads, group_lds_bytes(E), stream>>>(
             r.topk_idx, info, n, E, block_rows, max_blocks, r);

@@ -111,7 +111,7 @@ typedef struct {
 
 /* Version of this ABI (bumped on any change of a signature or of a call's
  * requirements, such as the workspace it needs; 4: moe_route takes a
- * workspace for k = 8 above 64 tokens). */
+ * workspace for k = 4, 8 or 16 above 64 tokens). */
 int moe_abi_version(void);
 
 /* Human-readable text of a status code (static string; never NULL). */
@@ -121,11 +121,11 @@ const char* moe_status_str(int status);
  * block_expert / block_row.  Returns a negative status on bad shapes. */
 int moe_route_max_blocks(int T, int E, int k, int block_rows);
 
-/* Device workspace bytes moe_route needs (0 on bad shapes).  With k = 8 and
- * T above the one-launch size (T > 64, or a one-launch LDS need above 64 KB)
- * it is T*k 32-bit words, rounded up to 256 bytes: the top-k pass records
- * each 64-assignment chunk's match information there for the grouping pass.
- * Otherwise it is 0 and ws may be NULL. */
+/* Device workspace bytes moe_route needs (0 on bad shapes).  With k = 4, 8 or
+ * 16 and T above the one-launch size (T > 64, or a one-launch LDS need above
+ * 64 KB) it is T*k 32-bit words, rounded up to 256 bytes: the top-k pass
+ * records each 64-assignment chunk's match information there for the
+ * grouping pass.  Otherwise it is 0 and ws may be NULL. */
 size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows);
 
 /* GPU-resident routing ([P1] "Prefill optimizations", GPU-resident routing

@@ -41,11 +41,14 @@ def test_max_blocks_and_workspace_sizes():
     assert bq.route_max_blocks(1, 256, 8, 32) == 1 + 8
     assert bq.route_max_blocks(64, 16, 2, 32) == 4 + 16
     assert bq.lib().moe_route_max_blocks(1, 256, 8, 48) == bq.MOE_ERR_SHAPE
-    # k = 8 above the one-launch size: T*k words of per-chunk match information
+    # k = 4, 8, 16 above the one-launch size: T*k words of per-chunk match information
     assert bq.route_workspace_bytes(512, 256, 8, 32) == 512 * 8 * 4
+    assert bq.route_workspace_bytes(512, 256, 4, 32) == 512 * 4 * 4
+    assert bq.route_workspace_bytes(512, 256, 16, 32) == 512 * 16 * 4
     assert bq.route_workspace_bytes(65, 256, 8, 32) == 9 * 256   # 65 * 8 words, rounded up to 256 bytes
     assert bq.route_workspace_bytes(64, 256, 8, 32) == 0     # one launch, no workspace
-    assert bq.route_workspace_bytes(512, 256, 4, 32) == 0    # other k: no workspace
+    assert bq.route_workspace_bytes(512, 256, 2, 32) == 0    # other k: no workspace
+    assert bq.route_workspace_bytes(512, 256, 6, 32) == 0
     assert bq.route_workspace_bytes(0, 256, 8, 32) == 0
     # h (T*k x I) + shared h (T x I_sh), bf16
     assert bq.gemm_workspace_bytes(512, 2048, 512, 512, 256, 8, 32) >= 512 * 8 * 512 * 2 + 512 * 512 * 2

@@ -70,22 +70,26 @@ def test_route_ties(T, E, k, levels, seed):
     assert_routing_matches(gpu_route(L, k, 32), L, k, 32)
 
 
-@pytest.mark.parametrize("T,E,levels,br,seed", [
-    (65, 256, 3, 32, 11),      # one token in the last 8-token chunk
-    (72, 8, 1, 32, 12),        # E = k = 8: every expert 8 times in every chunk
-    (129, 1000, 4, 16, 13),    # E up to 1000
-    (1000, 256, 2, 64, 14),    # heavy ties, 64-row blocks
-    (3000, 256, 5, 32, 15),    # more than 16 chunks per grouping wave: batched reloads
-    (4097, 64, 3, 16, 16),     # ragged tail over many batches
+@pytest.mark.parametrize("T,E,k,levels,br,seed", [
+    (65, 256, 8, 3, 32, 11),      # one token in the last 8-token chunk
+    (72, 8, 8, 1, 32, 12),        # E = k = 8: every expert 8 times in every chunk
+    (129, 1000, 8, 4, 16, 13),    # E up to 1000
+    (1000, 256, 8, 2, 64, 14),    # heavy ties, 64-row blocks
+    (3000, 256, 8, 5, 32, 15),    # more than 16 chunks per grouping wave: batched reloads
+    (4097, 64, 8, 3, 16, 16),     # ragged tail over many batches
+    (70, 128, 4, 3, 32, 17),      # k = 4: 16 tokens per top-k workgroup, partial last chunk
+    (5000, 64, 4, 2, 16, 18),     # k = 4 with batched reloads
+    (67, 300, 16, 3, 32, 19),     # k = 16: 4 tokens per top-k workgroup, E not a multiple of 64
+    (1500, 16, 16, 1, 64, 20),    # k = E = 16: every expert 4 times in every chunk
 ])
-def test_route_chunk_match_path(T, E, levels, br, seed):
-    """k = 8 above 64 tokens: the top-k pass records each 64-assignment chunk's
-    match information and the grouping pass uses it (route workspace of T*k
-    words); the routing arrays must still match the oracle bit for bit."""
-    assert bq.route_workspace_bytes(T, E, 8, br) >= T * 8 * 4
+def test_route_chunk_match_path(T, E, k, levels, br, seed):
+    """k = 4, 8, 16 above 64 tokens: the top-k pass records each 64-assignment
+    chunk's match information and the grouping pass uses it (route workspace of
+    T*k words); the routing arrays must still match the oracle bit for bit."""
+    assert bq.route_workspace_bytes(T, E, k, br) >= T * k * 4
     L = _tie_heavy(T, E, levels, seed)
-    announce(f"route chunk path T={T} E={E} levels={levels} br={br}")
-    assert_routing_matches(gpu_route(L, 8, br), L, 8, br)
+    announce(f"route chunk path T={T} E={E} k={k} levels={levels} br={br}")
+    assert_routing_matches(gpu_route(L, k, br), L, k, br)
 
 
 def test_route_all_equal_and_signed_zero():
