@@ -297,6 +297,7 @@ def test_fused_decode_sequential_equals_single(big_layer):
     (256, 1024, 64, 16, 768),    # k + 1 > 12 experts per down workgroup, K of down > 512
     (4096, 64, 8, 2, 64),        # H > 2048: several K passes per gate/up row
     (128, 128, 256, 64, 128),    # the largest k
+    (64, 64, 1000, 20, 64),      # the largest E (16 logits per lane), k > 16, smallest H and I
 ])
 def test_fused_decode_small_shapes(H, I, E, k, I_sh):
     cfg = small_config(6, H, I, E, k, I_sh, seed=E + k)
