@@ -80,6 +80,7 @@ SMALL = [
     (70, 384, 128, 8, 2, 128, 32),        # down columns: a partial second group of 256
     (301, 256, 128, 4, 2, 128, 32),       # ~150 rows per expert: 64-row down items (block pairs)
     (3000, 256, 128, 64, 8, 128, 32),     # one call above 2048 tokens: batched routing reloads
+    (200, 128, 64, 4, 4, 64, 32),         # paired down items with I = 64; k = 4 chunk routing
     (1, 2048, 512, 256, 8, 512, 32),      # batch-1 decode shape
     (9, 128, 64, 4, 4, 64, 16),           # k = E
     (50, 64, 64, 1000, 20, 64, 32),       # smallest H and I, largest E, k > 16 (radix top-k)
