@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500,
                     help="untimed steps first; the GPU needs about 30 ms of work to reach its steady clock")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="wall time of back-to-back calls before each timed line (clock ramp)")
     ap.add_argument("--block-rows", type=int, default=32)
     ap.add_argument("--layout", choices=("tiles", "rows"), default="tiles",
                     help="code-word layout of the timed layer: tile-packed (load-time "
@@ -230,6 +232,59 @@ def sweep(args, torch, bq, dev):
     print(json.dumps(out))
 
 
+def decode_launch_shapes(c):
+    """(grid, threads) of moe_decode_q4's two launches for a layer config."""
+    rows_per_wg = 4 * 2                       # 4 waves x 2 gate/up row pairs
+    gateup = (-(-(c.I_sh + c.k * c.I) // rows_per_wg), 256)
+    down = (c.H // 4, 512)                    # 4 output columns per workgroup, 8 waves
+    return [list(gateup), list(down)]
+
+
+def oracle_baselines(w_big, only, no_extra):
+    """The CPU oracle (numpy fp64) timed on this host, one bounded sample per
+    workload, about 20-30 s in all; tokens/s = tokens of the sample / its time."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from workload import CONFIGS, make_activations, make_weights
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
+                             if p.get("user_api") == "blas"})) or None
+    common = {"unit": "tokens/s", "cores": threads, "kind": "oracle", "blas": blas,
+              "host_cpus": len(os.sched_getaffinity(0))}
+
+    def run(w, xb, lg, k):
+        t0 = time.perf_counter()
+        oracle.moe_layer(xb, lg, w.gate, w.up, w.down, k, w.sh_gate, w.sh_up, w.sh_down)
+        return time.perf_counter() - t0
+
+    out = {}
+    names = ["prefill512"]
+    if not no_extra:
+        names += [n for n in ("tiny", "prefill2048", "decode", "skew8192") if not only or n in only]
+    for name in names:
+        c = CONFIGS[name]
+        w = make_weights(c, seed=0) if name == "tiny" else w_big
+        xb, lg = make_activations(c)
+        if name == "decode":      # single-token calls, as the GPU line runs them
+            n = 10
+            dt = sum(run(w, xb[t:t + 1], lg[t:t + 1], c.k) for t in range(n))
+            sample = f"the first {n} of the 1000 tokens, one single-token layer call each"
+        elif name == "skew8192":  # one bounded chunk
+            n = c.chunk
+            dt = run(w, xb[:n], lg[:n], c.k)
+            sample = f"the first {n}-token chunk of the 8192 tokens (one of the four chunk calls)"
+        else:
+            n = c.T
+            dt = run(w, xb, lg, c.k)
+            sample = f"one full {n}-token layer call"
+        out[name] = dict(common, value=n / dt, seconds=dt,
+                         sample=f"{sample} ({dt:.1f} s; numpy fp64, BLAS threads {threads}, "
+                                f"elementwise work single-threaded)")
+        log(f"cpu oracle {name}: {dt:.2f} s for {n} tokens ({n/dt:,.1f} tok/s)")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -287,7 +342,11 @@ def main():
     # ---------------- headline: prefill 512 ----------------
     x, lg = prep(cfg)
     T = cfg.T
+    # the clocks need tens of ms of back-to-back work to reach their steady state, more
+    # than a few warm-up calls give: settle on wall time first, then the counted warm-up
+    settle(lambda: layer.forward(x, lg), torch, ms=args.settle_ms)
     ms = timed(lambda: layer.forward(x, lg), args.steps, args.warmup, torch)
+    settle(cold(lambda L: L.forward(x, lg)), torch, ms=args.settle_ms)
     ms_cold = timed(cold(lambda L: L.forward(x, lg)), args.steps, args.warmup, torch)
     # per-call durations (events around each call) for the median
     per_call = []
@@ -342,6 +401,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -360,6 +420,7 @@ def main():
                      "measured_read_ceiling": ceiling / 1e9,
                      "frac_of_measured_ceiling": achieved / ceiling},
         "device": device_facts(torch, dev),
+        "library": bq.lib_fingerprint(),
         "layer": {"route_us": t_route * 1e6, "gateup_us": t_gu * 1e6, "down_us": t_dn * 1e6,
                   "combine_us": t_comb * 1e6, "touched_experts": touched,
                   "algorithmic_bytes": layer_bytes, "algorithmic_flops": flops,
@@ -453,6 +514,18 @@ def main():
     # ---------------- secondary workloads ----------------
     only = only_set(args)
     if not args.no_extra:
+        if not only or "tiny" in only:
+            c = CONFIGS["tiny"]
+            wt = make_weights(c, seed=0)
+            tiny = bq.MoeLayer(wt, c.H, c.I, c.I_sh, c.E, c.k, dev, prepack=True)
+            xt, lgt = prep(c)
+            settle(lambda: tiny.forward(xt, lgt), torch)
+            mst = timed(lambda: tiny.forward(xt, lgt), max(20, args.steps), 10, torch)
+            extra["tiny"] = {"tokens_per_s": c.T / (mst * 1e-3), "us_per_call": mst * 1e3,
+                             "what": "T 64, H 256, I 128, 16 experts top-2 + shared I 128: "
+                                     "launch-bound (four kernels for 1 MB of weights)"}
+            log(f"tiny: {mst*1e3:.1f} us/call, {c.T/(mst*1e-3):,.0f} tok/s")
+            del tiny
         if not only or "prefill2048" in only:
             c = CONFIGS["prefill2048"]
             x2, lg2 = prep(c)
@@ -522,7 +595,24 @@ def main():
             settle(graph.replay, torch)
             t_cold = timed(graph.replay, 3, 1, torch) * 1e-3 / c.T
             del graph
+            # the floor under per-token launches: the same chain of 2 launches per token with
+            # the decode kernels' grid shapes, empty, then with one dependent read each
+            pb = torch.zeros(3, dtype=torch.int32, device=dev)
+            shapes = decode_launch_shapes(c)
+            floor = {}
+            for dep in (False, True):
+                run = lambda: bq.moe_launch_probe(pb, 2 * c.T, *shapes, dep)  # noqa: E731
+                settle(run, torch, ms=50.0)
+                floor[dep] = timed(run, 3, 1, torch) * 1e-3 / c.T
+            extra_floor = {"empty_us_per_token": floor[False] * 1e6,
+                           "dependent_us_per_token": floor[True] * 1e6,
+                           "launch_shapes": shapes,
+                           "what": "2 launches per token with the decode kernels' grids: empty, "
+                                   "then each reading the word the previous launch wrote"}
+            log(f"decode floor: {floor[False]*1e6:.2f} us/token empty launches, "
+                f"{floor[True]*1e6:.2f} with one dependent read per launch")
             extra["decode"] = {"tokens_per_s": 1.0 / t_tok, "us_per_token": t_tok * 1e6,
+                               "launch_floor": extra_floor,
                                "hbm_frac": by_tok / t_tok / HBM_PEAK,
                                "algorithmic_bytes_per_token": by_tok,
                                "path": "moe_decode_q4: two launches per token "
@@ -551,24 +641,12 @@ def main():
                 f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%")
     result["extra"] = extra
 
-    # ---------------- CPU oracle baseline (rank 0, N = 1) ----------------
+    # ---------------- CPU oracle baselines (rank 0, N = 1) ----------------
     if not args.no_cpu_baseline:
-        import oracle
-        from threadpoolctl import threadpool_info
-        xb, lgn = make_activations(cfg)
-        t0 = time.perf_counter()
-        oracle.moe_layer(xb, lgn, w.gate, w.up, w.down, cfg.k, w.sh_gate, w.sh_up, w.sh_down)
-        dt = time.perf_counter() - t0
-        pools = threadpool_info()
-        threads = max([p.get("num_threads", 1) for p in pools] or [1])
-        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
-                                 if p.get("user_api") == "blas"})) or None
-        result["cpu_baseline"] = {
-            "value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
-            "sample": f"one full 512-token layer call of the same workload ({dt:.1f} s; numpy fp64, "
-                      f"BLAS threads {threads}, elementwise work single-threaded)"}
-        log(f"cpu oracle: {dt:.1f} s for 512 tokens")
+        base = oracle_baselines(w, only, args.no_extra)
+        result["cpu_baseline"] = base.pop("prefill512")
+        for name, b in base.items():
+            extra.setdefault(name, {})["cpu_baseline"] = b
     print(json.dumps(result))
 
 

@@ -13,8 +13,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# MOE_Q4_LIB may name another build of the same library (e.g. other tile sizes)
-LIB_PATH = os.environ.get("MOE_Q4_LIB") or os.path.join(HERE, "libmoe_q4.so")
+# the in-tree build of build.py; no other library can be substituted
+LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
 
 MOE_OK = 0
 MOE_ERR_NULL = -1
@@ -77,6 +77,7 @@ _SIGNATURES = {
                              + [_P] * 2 + [_P, _P, _P, _S, _P]),
     "moe_read_probe_sink_words": (_S, [_S]),
     "moe_read_probe": (_I, [_P, _S, _P, _S, _P]),
+    "moe_launch_probe": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
     "moe_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_decode_q4": (_I, [_P, _P, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(MoeQ4Mat)] * 6
                       + [ctypes.POINTER(MoeRouting), _P, _P, _S, _P]),
@@ -106,6 +107,14 @@ def lib():
     return _lib
 
 
+def lib_fingerprint() -> dict:
+    """Path and SHA-256 (first 16 hex digits) of the library this process loads."""
+    import hashlib
+    with open(LIB_PATH, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    return {"path": LIB_PATH, "sha256_16": digest}
+
+
 def status_str(status: int) -> str:
     return lib().moe_status_str(status).decode()
 
@@ -116,7 +125,86 @@ def _check(status: int, where: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of t for the C call (None for None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"arguments must be device tensors (got a tensor on {t.device})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# Argument checks.  The C ABI sees only pointers and sizes, so a tensor of the
+# wrong dtype, shape or layout, or routing arrays built for another call,
+# would reach the kernels as out-of-range addresses.  These checks run before
+# any C call; they raise TypeError (dtype) or ValueError (everything else).
+# ---------------------------------------------------------------------------
+
+def _tensor(t, name, dtype=None, shape=None):
+    """t must be a contiguous device tensor, of `dtype` and `shape` when given."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t     # the device is checked when the address is taken (_ptr, _mat, _rt)
+
+
+def _opt_tensor(t, name, present: bool, dtype=None, shape=None):
+    """t is required when `present`, and must be None otherwise."""
+    if not present:
+        if t is not None:
+            raise ValueError(f"{name}: must be None here")
+        return None
+    if t is None:
+        raise ValueError(f"{name}: required")
+    return _tensor(t, name, dtype, shape)
+
+
+def _ws(t, name="ws"):
+    """A workspace: any contiguous device tensor (its byte size is checked by the library)."""
+    return _tensor(t, name)
+
+
+def _routing_for(r, name, T, E, k, block_rows):
+    if not isinstance(r, DeviceRouting):
+        raise TypeError(f"{name}: expected a DeviceRouting")
+    if (r.T, r.E, r.k, r.block_rows) != (T, E, k, block_rows):
+        raise ValueError(f"{name}: built for T={r.T} E={r.E} k={r.k} block_rows={r.block_rows}, "
+                         f"the call has T={T} E={E} k={k} block_rows={block_rows}")
+    return r
+
+
+def _qmat_for(m, name, n_exp, N, K, present=True):
+    if not present:
+        if m is not None:
+            raise ValueError(f"{name}: must be None here")
+        return None
+    if not isinstance(m, DeviceQMat):
+        raise TypeError(f"{name}: expected a DeviceQMat")
+    if K % 64 or (m.codes.shape, m.scales.shape, m.biases.shape) != (
+            (n_exp, N, K // 8), (n_exp, N, K // 64), (n_exp, N, K // 64)):
+        raise ValueError(f"{name}: codes {tuple(m.codes.shape)}, scales {tuple(m.scales.shape)}, "
+                         f"biases {tuple(m.biases.shape)} do not hold a [{n_exp}, {N}, {K}] set")
+    for part in ("codes", "scales", "biases"):
+        _tensor(getattr(m, part), f"{name}.{part}")
+    return m
+
+
+def _expert_mats(gate, up, down, sh_gate, sh_up, sh_down, E, H, I, I_sh):
+    """Check the six matrix sets of a layer (down or the gate/up pair may be skipped by
+    passing False for them)."""
+    if gate is not False:
+        _qmat_for(gate, "gate", E, I, H)
+        _qmat_for(up, "up", E, I, H)
+        _qmat_for(sh_gate, "sh_gate", 1, I_sh, H, present=I_sh > 0)
+        _qmat_for(sh_up, "sh_up", 1, I_sh, H, present=I_sh > 0)
+    if down is not False:
+        _qmat_for(down, "down", E, H, I)
+        _qmat_for(sh_down, "sh_down", 1, H, I_sh, present=I_sh > 0)
 
 
 def _stream(stream, device):
@@ -208,24 +296,53 @@ def layer_workspace_bytes(chunk_tokens, H, I, I_sh, E, k, block_rows) -> int:
     return lib().moe_layer_workspace_bytes(chunk_tokens, H, I, I_sh, E, k, block_rows)
 
 
+BF16, F32, I32 = torch.bfloat16, torch.float32, torch.int32
+
+
 def moe_route(logits: torch.Tensor, k: int, block_rows: int, routing: DeviceRouting,
               ws: torch.Tensor, stream=None):
+    _tensor(logits, "logits", F32)
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [T, E]")
     T, E = logits.shape
-    _check(lib().moe_route(_ptr(logits), T, E, k, block_rows, ctypes.byref(routing.struct),
+    _routing_for(routing, "routing", T, E, k, block_rows)
+    _ws(ws, "route_ws")
+    _check(lib().moe_route(_ptr(logits), T, E, k, block_rows, _rt(routing),
                            _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream, logits.device)), "moe_route")
 
 
 def _mat(m):
-    return None if m is None else ctypes.byref(m.struct)
+    if m is None:
+        return None
+    for part in (m.codes, m.scales, m.biases):
+        _ptr(part)
+    return ctypes.byref(m.struct)
+
+
+def _rt(r):
+    _ptr(r.topk_idx)
+    return ctypes.byref(r.struct)
+
+
+def _x_of(x):
+    _tensor(x, "x", BF16)
+    if x.dim() != 2:
+        raise ValueError("x: expected [T, H]")
+    return x.shape
 
 
 def moe_grouped_gemm_q4(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, block_rows: int,
                         routing: DeviceRouting, gate, up, down, sh_gate, sh_up, sh_down,
                         expert_out: torch.Tensor, shared_out, ws: torch.Tensor, stream=None):
-    T, H = x.shape
+    T, H = _x_of(x)
+    _routing_for(routing, "routing", T, E, k, block_rows)
+    _expert_mats(gate, up, down, sh_gate, sh_up, sh_down, E, H, I, I_sh)
+    _tensor(expert_out, "expert_out", BF16, (T * k, H))
+    _opt_tensor(shared_out, "shared_out", I_sh > 0, BF16, (T, H))
+    _ws(ws)
     _check(lib().moe_grouped_gemm_q4(
-        _ptr(x), T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct),
+        _ptr(x), T, H, I, I_sh, E, k, block_rows, _rt(routing),
         _mat(gate), _mat(up), _mat(down), _mat(sh_gate), _mat(sh_up), _mat(sh_down),
         _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, x.device)), "moe_grouped_gemm_q4")
@@ -234,9 +351,12 @@ def moe_grouped_gemm_q4(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, bloc
 def moe_expert_gateup_q4(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, block_rows: int,
                          routing: DeviceRouting, gate, up, sh_gate, sh_up, ws: torch.Tensor,
                          stream=None):
-    T, H = x.shape
+    T, H = _x_of(x)
+    _routing_for(routing, "routing", T, E, k, block_rows)
+    _expert_mats(gate, up, False, sh_gate, sh_up, None, E, H, I, I_sh)
+    _ws(ws)
     _check(lib().moe_expert_gateup_q4(
-        _ptr(x), T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct),
+        _ptr(x), T, H, I, I_sh, E, k, block_rows, _rt(routing),
         _mat(gate), _mat(up), _mat(sh_gate), _mat(sh_up), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, x.device)), "moe_expert_gateup_q4")
 
@@ -244,8 +364,13 @@ def moe_expert_gateup_q4(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, blo
 def moe_expert_down_q4(T: int, H: int, I: int, I_sh: int, E: int, k: int, block_rows: int,
                        routing: DeviceRouting, down, sh_down, expert_out: torch.Tensor, shared_out,
                        ws: torch.Tensor, stream=None):
+    _routing_for(routing, "routing", T, E, k, block_rows)
+    _expert_mats(False, None, down, None, None, sh_down, E, H, I, I_sh)
+    _tensor(expert_out, "expert_out", BF16, (T * k, H))
+    _opt_tensor(shared_out, "shared_out", I_sh > 0, BF16, (T, H))
+    _ws(ws)
     _check(lib().moe_expert_down_q4(
-        T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct), _mat(down), _mat(sh_down),
+        T, H, I, I_sh, E, k, block_rows, _rt(routing), _mat(down), _mat(sh_down),
         _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, expert_out.device)), "moe_expert_down_q4")
 
@@ -254,11 +379,19 @@ def moe_layer_q4(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, E: in
                  block_rows: int, routing: DeviceRouting, route_ws: torch.Tensor, gate, up, down,
                  sh_gate, sh_up, sh_down, expert_out: torch.Tensor, shared_out,
                  gemm_ws: torch.Tensor, y: torch.Tensor, stream=None):
-    T, H = x.shape
+    T, H = _x_of(x)
+    _tensor(logits, "logits", F32, (T, E))
+    _routing_for(routing, "routing", T, E, k, block_rows)
+    _expert_mats(gate, up, down, sh_gate, sh_up, sh_down, E, H, I, I_sh)
+    _tensor(expert_out, "expert_out", BF16, (T * k, H))
+    _opt_tensor(shared_out, "shared_out", I_sh > 0, BF16, (T, H))
+    _tensor(y, "y", BF16, (T, H))
+    _ws(route_ws, "route_ws")
+    _ws(gemm_ws, "gemm_ws")
     _check(lib().moe_layer_q4(
         _ptr(x), _ptr(logits), T, H, I, I_sh, E, k, block_rows,
         _mat(gate), _mat(up), _mat(down), _mat(sh_gate), _mat(sh_up), _mat(sh_down),
-        ctypes.byref(routing.struct), _ptr(route_ws), route_ws.numel() * route_ws.element_size(),
+        _rt(routing), _ptr(route_ws), route_ws.numel() * route_ws.element_size(),
         _ptr(expert_out), _ptr(shared_out), _ptr(gemm_ws),
         gemm_ws.numel() * gemm_ws.element_size(), _ptr(y), _stream(stream, x.device)),
         "moe_layer_q4")
@@ -266,8 +399,16 @@ def moe_layer_q4(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, E: in
 
 def moe_combine(expert_out: torch.Tensor, shared_out, routing: DeviceRouting, k: int,
                 y: torch.Tensor, stream=None):
+    _tensor(y, "y", BF16)
+    if y.dim() != 2:
+        raise ValueError("y: expected [T, H]")
     T, H = y.shape
-    _check(lib().moe_combine(_ptr(expert_out), _ptr(shared_out), ctypes.byref(routing.struct),
+    if not isinstance(routing, DeviceRouting) or (routing.T, routing.k) != (T, k):
+        raise ValueError("routing: not built for this call's T and k")
+    _tensor(expert_out, "expert_out", BF16, (T * k, H))
+    if shared_out is not None:
+        _tensor(shared_out, "shared_out", BF16, (T, H))
+    _check(lib().moe_combine(_ptr(expert_out), _ptr(shared_out), _rt(routing),
                              T, H, k, _ptr(y), _stream(stream, y.device)), "moe_combine")
 
 
@@ -275,6 +416,10 @@ def moe_dequant_q4_bf16(m: DeviceQMat, n_exp: int, N: int, K: int, out: torch.Te
                         stream=None):
     """Expand a 4-bit matrix set [n_exp, N, K] into bf16 `out` [n_exp, N, K]; experts with
     counts[e] == 0 are skipped when counts (device int32 [n_exp]) is given."""
+    _qmat_for(m, "m", n_exp, N, K)
+    _tensor(out, "out", BF16, (n_exp, N, K))
+    if counts is not None:
+        _tensor(counts, "counts", I32, (n_exp,))
     _check(lib().moe_dequant_q4_bf16(ctypes.byref(m.struct), n_exp, N, K, _ptr(counts), _ptr(out),
                                      _stream(stream, out.device)), "moe_dequant_q4_bf16")
 
@@ -283,9 +428,15 @@ def moe_expert_gateup_bf16(x: torch.Tensor, I: int, I_sh: int, E: int, k: int, b
                            routing: DeviceRouting, gate, up, sh_gate, sh_up, ws: torch.Tensor,
                            stream=None):
     """moe_expert_gateup_q4 over bf16 weight tensors (gate/up [E, I, H], shared [1, I_sh, H])."""
-    T, H = x.shape
+    T, H = _x_of(x)
+    _routing_for(routing, "routing", T, E, k, block_rows)
+    _tensor(gate, "gate", BF16, (E, I, H))
+    _tensor(up, "up", BF16, (E, I, H))
+    _opt_tensor(sh_gate, "sh_gate", I_sh > 0, BF16, (1, I_sh, H))
+    _opt_tensor(sh_up, "sh_up", I_sh > 0, BF16, (1, I_sh, H))
+    _ws(ws)
     _check(lib().moe_expert_gateup_bf16(
-        _ptr(x), T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct),
+        _ptr(x), T, H, I, I_sh, E, k, block_rows, _rt(routing),
         _ptr(gate), _ptr(up), _ptr(sh_gate), _ptr(sh_up), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, x.device)), "moe_expert_gateup_bf16")
 
@@ -294,8 +445,14 @@ def moe_expert_down_bf16(T: int, H: int, I: int, I_sh: int, E: int, k: int, bloc
                          routing: DeviceRouting, down, sh_down, expert_out: torch.Tensor, shared_out,
                          ws: torch.Tensor, stream=None):
     """moe_expert_down_q4 over bf16 weight tensors (down [E, H, I], shared [1, H, I_sh])."""
+    _routing_for(routing, "routing", T, E, k, block_rows)
+    _tensor(down, "down", BF16, (E, H, I))
+    _opt_tensor(sh_down, "sh_down", I_sh > 0, BF16, (1, H, I_sh))
+    _tensor(expert_out, "expert_out", BF16, (T * k, H))
+    _opt_tensor(shared_out, "shared_out", I_sh > 0, BF16, (T, H))
+    _ws(ws)
     _check(lib().moe_expert_down_bf16(
-        T, H, I, I_sh, E, k, block_rows, ctypes.byref(routing.struct), _ptr(down), _ptr(sh_down),
+        T, H, I, I_sh, E, k, block_rows, _rt(routing), _ptr(down), _ptr(sh_down),
         _ptr(expert_out), _ptr(shared_out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, expert_out.device)), "moe_expert_down_bf16")
 
@@ -303,9 +460,17 @@ def moe_expert_down_bf16(T: int, H: int, I: int, I_sh: int, E: int, k: int, bloc
 def moe_combine_gated(expert_out: torch.Tensor, shared_out: torch.Tensor, shared_gate: torch.Tensor,
                       routing: DeviceRouting, k: int, y: torch.Tensor, stream=None):
     """moe_combine with the shared expert weighted per token by shared_gate (fp32 [T])."""
+    _tensor(y, "y", BF16)
+    if y.dim() != 2:
+        raise ValueError("y: expected [T, H]")
     T, H = y.shape
+    if not isinstance(routing, DeviceRouting) or (routing.T, routing.k) != (T, k):
+        raise ValueError("routing: not built for this call's T and k")
+    _tensor(expert_out, "expert_out", BF16, (T * k, H))
+    _tensor(shared_out, "shared_out", BF16, (T, H))
+    _tensor(shared_gate, "shared_gate", F32, (T,))
     _check(lib().moe_combine_gated(_ptr(expert_out), _ptr(shared_out), _ptr(shared_gate),
-                                   ctypes.byref(routing.struct), T, H, k, _ptr(y),
+                                   _rt(routing), T, H, k, _ptr(y),
                                    _stream(stream, y.device)), "moe_combine_gated")
 
 
@@ -313,8 +478,17 @@ def moe_router(x: torch.Tensor, w_router: torch.Tensor, logits: torch.Tensor, w_
                gate=None, stream=None):
     """logits [T, E] (fp32) = x [T, H] (bf16) @ w_router [E, H]^T; optionally
     gate [T] = sigmoid(x @ w_gate)."""
-    T, H = x.shape
+    T, H = _x_of(x)
+    _tensor(w_router, "w_router", BF16)
+    if w_router.dim() != 2 or w_router.shape[1] != H:
+        raise ValueError("w_router: expected [E, H]")
     E = w_router.shape[0]
+    _tensor(logits, "logits", F32, (T, E))
+    if (w_gate is None) != (gate is None):
+        raise ValueError("w_gate and gate: both given or both None")
+    if w_gate is not None:
+        _tensor(w_gate, "w_gate", BF16, (H,))
+        _tensor(gate, "gate", F32, (T,))
     _check(lib().moe_router(_ptr(x), T, H, _ptr(w_router), E, _ptr(w_gate), _ptr(logits),
                             _ptr(gate), _stream(stream, x.device)), "moe_router")
 
@@ -325,9 +499,21 @@ def read_probe_sink_words(nbytes: int) -> int:
 
 def moe_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     """Stream every byte of buf once; sink[i] = XOR of the uint32 words of 32 KB range i."""
+    _tensor(buf, "buf")
+    _tensor(sink, "sink")
     _check(lib().moe_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                 sink.numel() * sink.element_size() // 4,
                                 _stream(stream, buf.device)), "moe_read_probe")
+
+
+def moe_launch_probe(buf: torch.Tensor, n_launches: int, shape_a, shape_b, dep: bool,
+                     stream=None):
+    """n_launches kernels alternating (grid, threads) shape_a and shape_b; dep: each reads the
+    word the previous one wrote (buf: int32 [3] on the device)."""
+    _tensor(buf, "buf", I32, (3,))
+    _check(lib().moe_launch_probe(_ptr(buf), n_launches, shape_a[0], shape_a[1], shape_b[0],
+                                  shape_b[1], int(dep), _stream(stream, buf.device)),
+           "moe_launch_probe")
 
 
 def decode_workspace_bytes(H, I, I_sh, E, k) -> int:
@@ -337,22 +523,37 @@ def decode_workspace_bytes(H, I, I_sh, E, k) -> int:
 def moe_decode_q4(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
                   block_rows: int, gate, up, down, sh_gate, sh_up, sh_down, routing, y: torch.Tensor,
                   ws: torch.Tensor, stream=None):
-    """One token (x [1, H], logits [1, E]) through the whole layer in one launch."""
-    H = x.shape[1]
+    """One token (x [1, H], logits [1, E]) through the whole layer (two launches)."""
+    _, H = _x_of(x)
+    _tensor(x, "x", BF16, (1, H))
+    _tensor(logits, "logits", F32)
+    if logits.dim() != 2 or logits.shape[0] != 1:
+        raise ValueError("logits: expected [1, E]")
     E = logits.shape[1]
+    _expert_mats(gate, up, down, sh_gate, sh_up, sh_down, E, H, I, I_sh)
+    if routing is not None:
+        _routing_for(routing, "routing", 1, E, k, block_rows)
+    _tensor(y, "y", BF16, (1, H))
+    _ws(ws)
     _check(lib().moe_decode_q4(
         _ptr(x), _ptr(logits), H, I, I_sh, E, k, block_rows, _mat(gate), _mat(up), _mat(down),
         _mat(sh_gate), _mat(sh_up), _mat(sh_down),
-        None if routing is None else ctypes.byref(routing.struct), _ptr(y), _ptr(ws),
+        None if routing is None else _rt(routing), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream, x.device)), "moe_decode_q4")
 
 
 def moe_decode_q4_sequential(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
                              gate, up, down, sh_gate, sh_up, sh_down, y: torch.Tensor,
                              ws: torch.Tensor, stream=None):
-    """x [n, H], logits [n, E]: n single-token decode launches back to back."""
-    n, H = x.shape
+    """x [n, H], logits [n, E]: n single-token decode calls back to back."""
+    n, H = _x_of(x)
+    _tensor(logits, "logits", F32)
+    if logits.dim() != 2 or logits.shape[0] != n:
+        raise ValueError("logits: expected [n, E]")
     E = logits.shape[1]
+    _expert_mats(gate, up, down, sh_gate, sh_up, sh_down, E, H, I, I_sh)
+    _tensor(y, "y", BF16, (n, H))
+    _ws(ws)
     _check(lib().moe_decode_q4_sequential(
         _ptr(x), _ptr(logits), n, H, I, I_sh, E, k, _mat(gate), _mat(up), _mat(down),
         _mat(sh_gate), _mat(sh_up), _mat(sh_down), _ptr(y), _ptr(ws),
@@ -362,8 +563,14 @@ def moe_decode_q4_sequential(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh
 def moe_layer_chunked(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
                       block_rows: int, chunk_tokens: int, gate, up, down, sh_gate, sh_up,
                       sh_down, y: torch.Tensor, ws: torch.Tensor, stream=None):
-    T, H = x.shape
+    T, H = _x_of(x)
+    _tensor(logits, "logits", F32)
+    if logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError("logits: expected [T, E]")
     E = logits.shape[1]
+    _expert_mats(gate, up, down, sh_gate, sh_up, sh_down, E, H, I, I_sh)
+    _tensor(y, "y", BF16, (T, H))
+    _ws(ws)
     _check(lib().moe_layer_chunked(
         _ptr(x), _ptr(logits), T, H, I, I_sh, E, k, block_rows, chunk_tokens,
         _mat(gate), _mat(up), _mat(down), _mat(sh_gate), _mat(sh_up), _mat(sh_down),

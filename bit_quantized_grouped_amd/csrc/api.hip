@@ -1,6 +1,8 @@
 // C ABI of the 4-bit grouped MoE layer: host-side validation, workspace
-// layout and kernel dispatch.  Every entry point validates first and
-// enqueues nothing on failure; none allocates, frees or synchronises.
+// layout and kernel dispatch.  Every entry point checks all of its arguments
+// before its first launch and enqueues nothing when a check fails; none
+// allocates, frees or synchronises.  A multi-kernel call can still return
+// MOE_ERR_HIP from a later launch after its earlier kernels were enqueued.
 #include <initializer_list>
 #include <new>
 
@@ -514,10 +516,87 @@ int moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_wo
     }
 }
 
+int moe_launch_probe(uint32_t* buf, int n_launches, int grid_a, int threads_a, int grid_b,
+                     int threads_b, int dep, hipStream_t stream) {
+    try {
+        if (!buf) return MOE_ERR_NULL;
+        if (!aligned(buf, 4)) return MOE_ERR_ALIGN;
+        auto bad_shape = [](int g, int t) { return g < 1 || g > 65535 || t < 64 || t > 1024 || t % 64; };
+        if (n_launches < 1 || bad_shape(grid_a, threads_a) || bad_shape(grid_b, threads_b) ||
+            (dep != 0 && dep != 1))
+            return MOE_ERR_SHAPE;
+        return launch_launch_probe(buf, n_launches, grid_a, threads_a, grid_b, threads_b, dep,
+                                   stream) == hipSuccess
+                   ? MOE_OK
+                   : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k) {
     if (check_layer_shape(1, H, I, I_sh, E, k, 32) || k > 64) return 0;
     return decode_ws_layout(I, I_sh, k, nullptr, nullptr);
 }
+
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of one decode call (everything but the workspace); fills
+// the kernel arguments except the workspace pointers.
+int decode_args(const uint16_t* x, const float* logits, int H, int I, int I_sh, int E, int k,
+                int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
+                const moe_q4_mat* down, const moe_q4_mat* sh_gate, const moe_q4_mat* sh_up,
+                const moe_q4_mat* sh_down, const moe_routing* r, uint16_t* y, DecodeArgs* a) {
+    int st = check_layer_shape(1, H, I, I_sh, E, k, block_rows);
+    if (st) return st;
+    if (k > 64) return MOE_ERR_SHAPE;
+    if (!x || !logits || !y) return MOE_ERR_NULL;
+    if ((st = check_mat(gate)) || (st = check_mat(up)) || (st = check_mat(down))) return st;
+    if (I_sh) {
+        if ((st = check_mat(sh_gate)) || (st = check_mat(sh_up)) || (st = check_mat(sh_down)))
+            return st;
+    } else if (sh_gate || sh_up || sh_down) {
+        return MOE_ERR_SHAPE;
+    }
+    if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
+    if (r && (st = check_routing(r))) return st;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4)) return MOE_ERR_ALIGN;
+    *a = DecodeArgs{};
+    a->x = x;
+    a->logits = logits;
+    a->H = H;
+    a->I = I;
+    a->I_sh = I_sh;
+    a->E = E;
+    a->k = k;
+    a->gate = to_dev(gate);
+    a->up = to_dev(up);
+    a->down = to_dev(down);
+    a->sh_gate = to_dev(sh_gate);
+    a->sh_up = to_dev(sh_up);
+    a->sh_down = to_dev(sh_down);
+    a->write_routing = r ? 1 : 0;
+    if (r) a->r = to_dev(r);
+    a->max_blocks = max_blocks_of(1, E, k, block_rows);
+    a->y = y;
+    return MOE_OK;
+}
+
+// Points the decode kernels' workspace (h, then the chosen experts and their
+// weights) at ws.
+void decode_ws(DecodeArgs* a, void* ws) {
+    size_t off_idx = 0, off_w = 0;
+    decode_ws_layout(a->I, a->I_sh, a->k, &off_idx, &off_w);
+    a->h = (uint16_t*)ws;
+    a->sel_idx = (int32_t*)((char*)ws + off_idx);
+    a->sel_w = (float*)((char*)ws + off_w);
+}
+
+}  // namespace
+
+extern "C" {
 
 int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh, int E, int k,
                   int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
@@ -525,44 +604,12 @@ int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh
                   const moe_q4_mat* sh_down, const moe_routing* r, uint16_t* y, void* ws,
                   size_t ws_bytes, hipStream_t stream) {
     try {
-        int st = check_layer_shape(1, H, I, I_sh, E, k, block_rows);
+        DecodeArgs a;
+        int st = decode_args(x, logits, H, I, I_sh, E, k, block_rows, gate, up, down, sh_gate,
+                             sh_up, sh_down, r, y, &a);
         if (st) return st;
-        if (k > 64) return MOE_ERR_SHAPE;
-        if (!x || !logits || !y) return MOE_ERR_NULL;
-        if ((st = check_mat(gate)) || (st = check_mat(up)) || (st = check_mat(down))) return st;
-        if (I_sh) {
-            if ((st = check_mat(sh_gate)) || (st = check_mat(sh_up)) || (st = check_mat(sh_down)))
-                return st;
-        } else if (sh_gate || sh_up || sh_down) {
-            return MOE_ERR_SHAPE;
-        }
-        if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
-        if (r && (st = check_routing(r))) return st;
-        if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4)) return MOE_ERR_ALIGN;
-        size_t off_idx = 0, off_w = 0;
-        const size_t need = decode_ws_layout(I, I_sh, k, &off_idx, &off_w);
-        if ((st = check_ws(ws, ws_bytes, need))) return st;
-        DecodeArgs a{};
-        a.x = x;
-        a.logits = logits;
-        a.H = H;
-        a.I = I;
-        a.I_sh = I_sh;
-        a.E = E;
-        a.k = k;
-        a.gate = to_dev(gate);
-        a.up = to_dev(up);
-        a.down = to_dev(down);
-        a.sh_gate = to_dev(sh_gate);
-        a.sh_up = to_dev(sh_up);
-        a.sh_down = to_dev(sh_down);
-        a.write_routing = r ? 1 : 0;
-        if (r) a.r = to_dev(r);
-        a.max_blocks = max_blocks_of(1, E, k, block_rows);
-        a.h = (uint16_t*)ws;
-        a.sel_idx = (int32_t*)((char*)ws + off_idx);
-        a.sel_w = (float*)((char*)ws + off_w);
-        a.y = y;
+        if ((st = check_ws(ws, ws_bytes, decode_ws_layout(I, I_sh, k, nullptr, nullptr)))) return st;
+        decode_ws(&a, ws);
         return launch_decode(a, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     } catch (...) {
         return MOE_ERR_HIP;
@@ -600,7 +647,10 @@ int moe_layer_chunked(const uint16_t* x, const float* logits, int T, int H, int 
     try {
         if (chunk_tokens < 1) return MOE_ERR_SHAPE;
         const int C = chunk_tokens < T ? chunk_tokens : T;
-        int st = check_layer_shape(T, H, I, I_sh, E, k, block_rows);
+        // Every kernel works inside one chunk (x, logits and y are advanced on the
+        // host in size_t), so the 31-bit offset limits apply to the chunk; the whole
+        // prompt only needs a valid routing shape.
+        int st = check_route_shape(T, E, k, block_rows);
         if (st) return st;
         if ((st = check_layer_shape(C, H, I, I_sh, E, k, block_rows))) return st;
         if (!x || !logits || !y || !ws) return MOE_ERR_NULL;

@@ -85,6 +85,9 @@ hipError_t launch_combine(const uint16_t* expert_out, const uint16_t* shared_out
 // probe.hip: streaming-read probe, one sink word per 32 KB read
 size_t read_probe_sink_words(size_t bytes);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+// probe.hip: chains of empty or dependent launches (kernel-boundary cost)
+hipError_t launch_launch_probe(uint32_t* buf, int n_launches, int grid_a, int threads_a, int grid_b,
+                               int threads_b, int dep, hipStream_t stream);
 
 // router.hip
 hipError_t launch_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,

@@ -40,6 +40,31 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4_t
     }
 }
 
+// Launch-latency probe.  Kernel i of a chain reads word i % 2 of buf in every
+// workgroup and workgroup 0 writes that value + 1 into word (i + 1) % 2, so
+// each launch waits on the previous launch's write through memory, as the two
+// launches of a decode token do (h and the chosen experts cross the kernel
+// boundary).  With dep = 0 the kernels do nothing: the cost of the launches
+// and kernel boundaries alone.
+__global__ void launch_probe_kernel(uint32_t* buf, int src, int dep) {
+    if (!dep || threadIdx.x != 0) return;
+    const uint32_t v = __atomic_load_n(buf + src, __ATOMIC_RELAXED);
+    if (blockIdx.x == 0) buf[src ^ 1] = v + 1;
+    else if (v == 0xFFFFFFFFu) buf[2] = blockIdx.x;   // keeps every workgroup's read
+}
+
+hipError_t launch_launch_probe(uint32_t* buf, int n_launches, int grid_a, int threads_a, int grid_b,
+                               int threads_b, int dep, hipStream_t stream) {
+    for (int i = 0; i < n_launches; ++i) {
+        const bool a = (i & 1) == 0;
+        launch_probe_kernel<<<a ? grid_a : grid_b, a ? threads_a : threads_b, 0, stream>>>(buf, i & 1,
+                                                                                         dep);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 size_t read_probe_sink_words(size_t bytes) {
     const size_t n16 = bytes / 16;
     return (n16 + kProbePieces - 1) / kProbePieces;

@@ -25,9 +25,16 @@
  *     kernels on `stream`; it never allocates, frees or synchronises the
  *     host, and never reads device memory on the host.  Device-side values
  *     (such as n_blocks) stay on the device.
- *   - A failed call returns a negative status and enqueues nothing.  No C++
- *     exception crosses this boundary.  Device data (code words, scale
- *     values) is not validated.
+ *   - A call that fails its host-side checks returns a negative status and
+ *     enqueues nothing.  No C++ exception crosses this boundary.  Device
+ *     data (code words, scale values) is not validated.
+ *   - Calls that enqueue more than one kernel (moe_route above its
+ *     one-launch size, moe_grouped_gemm_q4, moe_layer_q4, moe_layer_chunked,
+ *     moe_decode_q4 and its variants) check every argument before the first
+ *     launch, but a launch itself can still fail (MOE_ERR_HIP, from
+ *     hipGetLastError) after earlier kernels of the same call were enqueued.
+ *     Those kernels then run; the call's outputs are undefined and the
+ *     caller should treat the stream as failed.
  *   - The library holds no mutable global state: calls on different streams
  *     may run concurrently from different threads if their buffers differ.
  *   - Shapes: 1 <= k <= E <= 1000; H, I, I_sh are multiples of 64 (I_sh = 0
@@ -288,6 +295,24 @@ size_t moe_read_probe_sink_words(size_t bytes);
 int moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
                    hipStream_t stream);
 
+/* Launch-latency probe (measurement only): the floor under a chain of
+ * dependent per-token launches such as moe_decode_q4's.  Enqueues n_launches
+ * kernels on `stream`, alternating two shapes (grid_a workgroups of threads_a
+ * threads, then grid_b of threads_b), the way a decode token's two launches
+ * alternate.
+ *   dep = 0: the kernels do nothing (launch and kernel-boundary cost only);
+ *   dep = 1: launch i reads word i % 2 of buf in every workgroup and its
+ *            workgroup 0 writes that value + 1 into word (i + 1) % 2, so each
+ *            launch waits on the previous one's write through memory; from
+ *            zeroed words, word n % 2 holds n after n launches.
+ *   buf: device, 3 uint32 words, 4-byte aligned (word 2 is never written in
+ *        practice: only when a read returns 0xFFFFFFFF).
+ * Grids 1..65535, threads 64..1024 in multiples of 64, n_launches >= 1.
+ * Status: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_SHAPE, MOE_ERR_HIP (a launch
+ * failed after the earlier ones of the chain were enqueued). */
+int moe_launch_probe(uint32_t* buf, int n_launches, int grid_a, int threads_a, int grid_b,
+                     int threads_b, int dep, hipStream_t stream);
+
 /* Device workspace bytes moe_decode_q4 needs (0 on bad shapes). */
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k);
 
@@ -335,7 +360,10 @@ size_t moe_layer_workspace_bytes(int chunk_tokens, int H, int I, int I_sh, int E
  * [c*chunk_tokens, ...) form independent layer calls (route, grouped GEMM,
  * combine) enqueued in order on `stream` with no host synchronisation.
  * All temporaries (routing, h, expert_out, shared_out) live in `ws` and are
- * sized for one chunk.  y bf16 [T, H]. */
+ * sized for one chunk.  y bf16 [T, H].
+ * Shapes: the size limits of the conventions above apply to one chunk
+ * (C = min(chunk_tokens, T) tokens), since every kernel works inside one
+ * chunk; the whole prompt needs only T*k < 2^30. */
 int moe_layer_chunked(const uint16_t* x, const float* logits, int T, int H, int I, int I_sh,
                       int E, int k, int block_rows, int chunk_tokens,
                       const moe_q4_mat* gate, const moe_q4_mat* up, const moe_q4_mat* down,

@@ -312,3 +312,22 @@ def test_layout_validation():
     assert pp(K=100) == bq.MOE_ERR_SHAPE
     assert pp(dst=FAKE) == bq.MOE_ERR_SHAPE                             # in place
     assert pp(dst=MISALIGNED) == bq.MOE_ERR_ALIGN
+
+
+def test_chunked_driver_checks_the_chunk_shape_not_the_prompt():
+    """A 131072-token prompt in chunks of 2048 (H 2048, k 8): T*k*H is 2^31, past the
+    one-call limit, but every kernel works inside one chunk, so validation passes and
+    the call stops only at the undersized workspace."""
+    L = bq.lib()
+    m = _mat()
+    mats = [ctypes.byref(m)] * 6
+    T, H, I, E, k = 131072, 2048, 512, 256, 8
+    assert bq.gemm_workspace_bytes(T, H, I, I, E, k, 32) == 0          # one call: too large
+    ws = bq.layer_workspace_bytes(2048, H, I, I, E, k, 32)
+    assert ws > 0
+    args = lambda T_, chunk, wsb: [FAKE, FAKE, T_, H, I, I, E, k, 32, chunk] + mats + [FAKE, FAKE, wsb, None]  # noqa: E731
+    assert L.moe_layer_chunked(*args(T, 2048, ws - 1)) == bq.MOE_ERR_WORKSPACE
+    # a chunk past the per-call limit is still rejected
+    assert L.moe_layer_chunked(*args(T, 65536, 1 << 40)) == bq.MOE_ERR_SHAPE
+    # the routing bound T*k < 2^30 holds for the whole prompt
+    assert L.moe_layer_chunked(*args(1 << 27, 2048, 1 << 40)) == bq.MOE_ERR_SHAPE
