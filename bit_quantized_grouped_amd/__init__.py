@@ -81,6 +81,9 @@ _SIGNATURES = {
     "moe_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "moe_decode_q4": (_I, [_P, _P, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(MoeQ4Mat)] * 6
                       + [ctypes.POINTER(MoeRouting), _P, _P, _S, _P]),
+    "moe_decode_noalloc_max_bytes": (_S, []),
+    "moe_decode_q4_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(MoeQ4Mat)] * 6
+                              + [ctypes.POINTER(MoeRouting), _P, _P]),
     "moe_decode_q4_sequential": (_I, [_P, _P, _I, _I, _I, _I, _I, _I]
                                  + [ctypes.POINTER(MoeQ4Mat)] * 6 + [_P, _P, _S, _P]),
     "moe_layer_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
@@ -540,6 +543,32 @@ def moe_decode_q4(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: i
         _mat(sh_gate), _mat(sh_up), _mat(sh_down),
         None if routing is None else _rt(routing), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream, x.device)), "moe_decode_q4")
+
+
+def decode_noalloc_max_bytes() -> int:
+    return lib().moe_decode_noalloc_max_bytes()
+
+
+def moe_decode_q4_noalloc(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,
+                          block_rows: int, gate, up, down, sh_gate, sh_up, sh_down, routing,
+                          y: torch.Tensor, stream=None):
+    """moe_decode_q4 with the library's device-resident scratch as its workspace (no
+    allocation; calls that overlap on one GPU race)."""
+    _, H = _x_of(x)
+    _tensor(x, "x", BF16, (1, H))
+    _tensor(logits, "logits", F32)
+    if logits.dim() != 2 or logits.shape[0] != 1:
+        raise ValueError("logits: expected [1, E]")
+    E = logits.shape[1]
+    _expert_mats(gate, up, down, sh_gate, sh_up, sh_down, E, H, I, I_sh)
+    if routing is not None:
+        _routing_for(routing, "routing", 1, E, k, block_rows)
+    _tensor(y, "y", BF16, (1, H))
+    _check(lib().moe_decode_q4_noalloc(
+        _ptr(x), _ptr(logits), H, I, I_sh, E, k, block_rows, _mat(gate), _mat(up), _mat(down),
+        _mat(sh_gate), _mat(sh_up), _mat(sh_down),
+        None if routing is None else _rt(routing), _ptr(y), _stream(stream, x.device)),
+        "moe_decode_q4_noalloc")
 
 
 def moe_decode_q4_sequential(x: torch.Tensor, logits: torch.Tensor, I: int, I_sh: int, k: int,

@@ -4,6 +4,7 @@
 // allocates, frees or synchronises.  A multi-kernel call can still return
 // MOE_ERR_HIP from a later launch after its earlier kernels were enqueued.
 #include <initializer_list>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe_q4.h"
@@ -594,6 +595,42 @@ void decode_ws(DecodeArgs* a, void* ws) {
     a->sel_w = (float*)((char*)ws + off_w);
 }
 
+// ---- scratch for moe_decode_q4_noalloc ----
+// A file-scope device array stands in for the workspace of callers that cannot
+// allocate.  In host code `decode_scratch` names a host-side stand-in, not a
+// device address: its device address is looked up once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+constexpr size_t kDecodeScratchBytes = 256 * 1024;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char decode_scratch[kDecodeScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of decode_scratch on the device that owns `stream`.
+hipError_t scratch_for(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(decode_scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -610,6 +647,29 @@ int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh
         if (st) return st;
         if ((st = check_ws(ws, ws_bytes, decode_ws_layout(I, I_sh, k, nullptr, nullptr)))) return st;
         decode_ws(&a, ws);
+        return launch_decode(a, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+size_t moe_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
+
+int moe_decode_q4_noalloc(const uint16_t* x, const float* logits, int H, int I, int I_sh, int E,
+                          int k, int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
+                          const moe_q4_mat* down, const moe_q4_mat* sh_gate,
+                          const moe_q4_mat* sh_up, const moe_q4_mat* sh_down,
+                          const moe_routing* r, uint16_t* y, hipStream_t stream) {
+    try {
+        DecodeArgs a;
+        int st = decode_args(x, logits, H, I, I_sh, E, k, block_rows, gate, up, down, sh_gate,
+                             sh_up, sh_down, r, y, &a);
+        if (st) return st;
+        if (decode_ws_layout(I, I_sh, k, nullptr, nullptr) > kDecodeScratchBytes)
+            return MOE_ERR_WORKSPACE;
+        void* scratch = nullptr;
+        if (scratch_for(stream, &scratch) != hipSuccess) return MOE_ERR_HIP;
+        decode_ws(&a, scratch);
         return launch_decode(a, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     } catch (...) {
         return MOE_ERR_HIP;

@@ -340,6 +340,32 @@ int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh
                   const moe_q4_mat* sh_down, const moe_routing* r, uint16_t* y, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 
+/* Largest workspace moe_decode_q4_noalloc can serve: the bytes of its
+ * device-resident scratch array (256 KiB). */
+size_t moe_decode_noalloc_max_bytes(void);
+
+/* moe_decode_q4 without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The two launches, their results and the
+ * status codes are those of moe_decode_q4; the workspace (h and the chosen
+ * experts) is instead a file-scope device array of the library, one per GPU,
+ * held until the process ends.  Its device address is looked up on the first
+ * call on each device (hipGetSymbolAddress); no call allocates or frees.
+ *   - Shapes whose moe_decode_workspace_bytes() exceeds
+ *     moe_decode_noalloc_max_bytes() return MOE_ERR_WORKSPACE (with k = 8
+ *     this allows max(I, I_sh) up to 14336).
+ *   - Every call on one GPU uses the same array: calls that overlap on one
+ *     GPU (different streams, or several host threads) race and give
+ *     undefined results.  Calls in one stream's order are safe.  Nothing in
+ *     the array needs to start at zero (each call writes what it reads).
+ *   - MOE_ERR_HIP also when the device of `stream` cannot be queried or the
+ *     array's address cannot be obtained. */
+int moe_decode_q4_noalloc(const uint16_t* x, const float* logits, int H, int I, int I_sh, int E,
+                          int k, int block_rows, const moe_q4_mat* gate, const moe_q4_mat* up,
+                          const moe_q4_mat* down, const moe_q4_mat* sh_gate,
+                          const moe_q4_mat* sh_up, const moe_q4_mat* sh_down,
+                          const moe_routing* r, uint16_t* y, hipStream_t stream);
+
 /* n_tok independent batch-1 decode calls, enqueued back to
  * back on `stream` (token t uses row t of x, logits and y; no batching across
  * tokens, no host synchronisation).  Same per-token result as moe_decode_q4
