@@ -537,7 +537,7 @@ int moe_launch_probe(uint32_t* buf, int n_launches, int grid_a, int threads_a, i
 
 size_t moe_decode_workspace_bytes(int H, int I, int I_sh, int E, int k) {
     if (check_layer_shape(1, H, I, I_sh, E, k, 32) || k > 64) return 0;
-    return decode_ws_layout(I, I_sh, k, nullptr, nullptr);
+    return decode_ws_layout(H, I, I_sh, k).total;
 }
 
 }  // extern "C"
@@ -588,11 +588,10 @@ int decode_args(const uint16_t* x, const float* logits, int H, int I, int I_sh, 
 // Points the decode kernels' workspace (h, then the chosen experts and their
 // weights) at ws.
 void decode_ws(DecodeArgs* a, void* ws) {
-    size_t off_idx = 0, off_w = 0;
-    decode_ws_layout(a->I, a->I_sh, a->k, &off_idx, &off_w);
-    a->h = (uint16_t*)ws;
-    a->sel_idx = (int32_t*)((char*)ws + off_idx);
-    a->sel_w = (float*)((char*)ws + off_w);
+    const DecodeWs L = decode_ws_layout(a->H, a->I, a->I_sh, a->k);
+    a->h = (uint16_t*)((char*)ws + L.h);
+    a->sel_idx = (int32_t*)((char*)ws + L.sel_idx);
+    a->sel_w = (float*)((char*)ws + L.sel_w);
 }
 
 // ---- scratch for moe_decode_q4_noalloc ----
@@ -645,7 +644,7 @@ int moe_decode_q4(const uint16_t* x, const float* logits, int H, int I, int I_sh
         int st = decode_args(x, logits, H, I, I_sh, E, k, block_rows, gate, up, down, sh_gate,
                              sh_up, sh_down, r, y, &a);
         if (st) return st;
-        if ((st = check_ws(ws, ws_bytes, decode_ws_layout(I, I_sh, k, nullptr, nullptr)))) return st;
+        if ((st = check_ws(ws, ws_bytes, decode_ws_layout(H, I, I_sh, k).total))) return st;
         decode_ws(&a, ws);
         return launch_decode(a, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     } catch (...) {
@@ -665,7 +664,7 @@ int moe_decode_q4_noalloc(const uint16_t* x, const float* logits, int H, int I, 
         int st = decode_args(x, logits, H, I, I_sh, E, k, block_rows, gate, up, down, sh_gate,
                              sh_up, sh_down, r, y, &a);
         if (st) return st;
-        if (decode_ws_layout(I, I_sh, k, nullptr, nullptr) > kDecodeScratchBytes)
+        if (decode_ws_layout(H, I, I_sh, k).total > kDecodeScratchBytes)
             return MOE_ERR_WORKSPACE;
         void* scratch = nullptr;
         if (scratch_for(stream, &scratch) != hipSuccess) return MOE_ERR_HIP;

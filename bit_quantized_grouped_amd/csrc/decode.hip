@@ -91,25 +91,34 @@ __device__ __forceinline__ float qdot32(const u32x4_t& w, const float (&f)[32]) 
     return a;
 }
 
+// One butterfly step over lane distance M for CNT values, then the next ones
+// (compile-time recursion, so v stays in registers; a run-time loop here
+// would index v dynamically and move it to shared memory).
+template <int CNT, int M, int NV>
+__device__ __forceinline__ void reduce_steps(float (&v)[NV], int lane) {
+    if constexpr (CNT > 1) {
+        const bool upper = (lane & M) != 0;
+#pragma unroll
+        for (int i = 0; i < CNT / 2; ++i) {
+            const float keep = upper ? v[i + CNT / 2] : v[i];
+            const float send = upper ? v[i] : v[i + CNT / 2];
+            v[i] = keep + shfl_xor(send, M);
+        }
+        reduce_steps<CNT / 2, M / 2>(v, lane);
+    }
+}
+
 // Butterfly reduction of NV values over the wave.  Afterwards every lane
 // holds the full sum of one value: the top log2(NV) lane bits, read from
 // bit 5 down, are the binary digits of that value's index (most significant
 // first).
 template <int NV>
 __device__ __forceinline__ float wave_reduce_multi(float (&v)[NV], int lane) {
-    int m = WAVE / 2;
-#pragma unroll
-    for (int cnt = NV; cnt > 1; cnt /= 2, m /= 2) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < cnt / 2; ++i) {
-            const float keep = upper ? v[i + cnt / 2] : v[i];
-            const float send = upper ? v[i] : v[i + cnt / 2];
-            v[i] = keep + shfl_xor(send, m);
-        }
-    }
+    static_assert(NV >= 1 && NV <= WAVE && (NV & (NV - 1)) == 0, "a power of two up to 64");
+    reduce_steps<NV, WAVE / 2>(v, lane);
     float s = v[0];
-    for (; m >= 1; m /= 2) s += shfl_xor(s, m);
+#pragma unroll
+    for (int m = WAVE / 2 / NV; m >= 1; m /= 2) s += shfl_xor(s, m);
     return s;
 }
 
@@ -218,6 +227,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
                 su[r] = bf16_to_f32(us[r][grp]);
                 bu[r] = bf16_to_f32(ub[r][grp]);
             }
+            // every load of the pass is issued before the first wait (the scheduler
+            // would otherwise interleave them with the math, one row per round trip)
+            __builtin_amdgcn_sched_barrier(0);
             float xf[32];
             const float sx = widen32(xv, xf);
 #pragma unroll
@@ -296,6 +308,7 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(DecodeArgs p) {
                     for (int q = 0; q < 4; ++q) hv[i][q] = u32x4_t{0, 0, 0, 0};
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < kDnExp; ++i) {
                 float hf[32];
@@ -317,21 +330,39 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(DecodeArgs p) {
     }
 }
 
-size_t decode_ws_layout(int I, int I_sh, int k, size_t* off_sel_idx, size_t* off_sel_w) {
+DecodeWs decode_ws_layout(int H, int I, int I_sh, int k) {
+    (void)H;
+    DecodeWs w{};
     const int ldh = I > I_sh ? I : I_sh;
-    const size_t h = align_up((size_t)(k + 1) * ldh * sizeof(uint16_t), 256);
-    if (off_sel_idx) *off_sel_idx = h;
-    if (off_sel_w) *off_sel_w = h + kDecMaxK * sizeof(int32_t);
-    return h + align_up(kDecMaxK * (sizeof(int32_t) + sizeof(float)), 256);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += align_up(bytes, 256);
+        return at;
+    };
+    w.h = take((size_t)(k + 1) * ldh * sizeof(uint16_t));
+    w.sel_idx = take(kDecMaxK * sizeof(int32_t));
+    w.sel_w = take(kDecMaxK * sizeof(float));
+    w.part = 0;
+    w.total = o;
+    return w;
+}
+
+void decode_launch_shapes(int H, int I, int I_sh, int k, int* grid1, int* threads1, int* grid2,
+                          int* threads2) {
+    const int chunks = (I_sh + k * I + kGuRows - 1) / kGuRows;
+    *grid1 = (chunks + kDecWaves - 1) / kDecWaves;
+    *threads1 = kDecThreads;
+    *grid2 = H / kDnCols;
+    *threads2 = kDnThreads;
 }
 
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
+    int g1, t1, g2, t2;
+    decode_launch_shapes(args.H, args.I, args.I_sh, args.k, &g1, &t1, &g2, &t2);
     const int epl = (args.E + WAVE - 1) / WAVE;
-    const int n_tasks = args.I_sh + args.k * args.I;
-    const int chunks = (n_tasks + kGuRows - 1) / kGuRows;
-    const dim3 gu_grid((chunks + kDecWaves - 1) / kDecWaves);
 #define MOE_DECODE_GU(N) \
-    hipLaunchKernelGGL(decode_gateup_kernel<N>, gu_grid, dim3(kDecThreads), 0, stream, args)
+    hipLaunchKernelGGL(decode_gateup_kernel<N>, dim3(g1), dim3(t1), 0, stream, args)
     if (epl <= 1) MOE_DECODE_GU(1);
     else if (epl <= 2) MOE_DECODE_GU(2);
     else if (epl <= 4) MOE_DECODE_GU(4);
@@ -340,8 +371,7 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
 #undef MOE_DECODE_GU
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_down_kernel, dim3(args.H / kDnCols), dim3(kDnThreads), 0, stream,
-                       args);
+    hipLaunchKernelGGL(decode_down_kernel, dim3(g2), dim3(t2), 0, stream, args);
     return hipGetLastError();
 }
 

@@ -68,13 +68,19 @@ struct DecodeArgs {
     RoutingDev r;
     int write_routing;
     int max_blocks;
-    uint16_t* h;              // workspace [k + 1][max(I, I_sh)] bf16
+    uint16_t* h;              // workspace [k + 1][max(I, I_sh)] bf16: SwiGLU activations per slot
     int32_t* sel_idx;         // workspace [k]: chosen experts, slot order
     float* sel_w;             // workspace [k]: their weights
     uint16_t* y;              // [1, H]
 };
-// Workspace bytes; offsets of sel_idx and sel_w (h is at offset 0).
-size_t decode_ws_layout(int I, int I_sh, int k, size_t* off_sel_idx, size_t* off_sel_w);
+// Workspace offsets (bytes) and size of one decode call.
+struct DecodeWs {
+    size_t h, sel_idx, sel_w, part, total;   // part: unused (0)
+};
+DecodeWs decode_ws_layout(int H, int I, int I_sh, int k);
+// (grid, threads) of the two decode launches.
+void decode_launch_shapes(int H, int I, int I_sh, int k, int* grid1, int* threads1, int* grid2,
+                          int* threads2);
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream);
 
 // combine.hip

@@ -23,18 +23,22 @@ __device__ __forceinline__ int wave_popc_ge(uint32_t key, uint32_t th, bool vali
 
 // Largest key over the wave, returned uniform.  DPP: row_shr 1, 2, 4, 8 leave
 // each row's maximum in its lane 15; row_bcast 15 and 31 carry those into
-// lane 63.  Lanes a shift does not reach keep their own value (max is
-// idempotent, so overlapping windows are harmless).
+// lane 63.  A lane whose source lies outside the wave or its row reads 0
+// (bound_ctrl), which max ignores (keys are unsigned), and extra rows taking
+// part in the broadcasts only take a max over windows that overlap: max is
+// idempotent, so every lane still holds a max of some lanes and lane 63 the
+// max of all.  The form lets the compiler fold each move into its max
+// (v_max_u32 with a DPP source), one instruction per step.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#define MOE_DPP_MAX(ctrl, rows)                                                           \
+#define MOE_DPP_MAX(ctrl)                                                                 \
     v = __builtin_elementwise_max(                                                        \
-        v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rows, 0xf, false))
-    MOE_DPP_MAX(0x111, 0xf);   // row_shr:1
-    MOE_DPP_MAX(0x112, 0xf);   // row_shr:2
-    MOE_DPP_MAX(0x114, 0xf);   // row_shr:4
-    MOE_DPP_MAX(0x118, 0xf);   // row_shr:8
-    MOE_DPP_MAX(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
-    MOE_DPP_MAX(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+        v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xf, 0xf, true))
+    MOE_DPP_MAX(0x111);   // row_shr:1
+    MOE_DPP_MAX(0x112);   // row_shr:2
+    MOE_DPP_MAX(0x114);   // row_shr:4
+    MOE_DPP_MAX(0x118);   // row_shr:8
+    MOE_DPP_MAX(0x142);   // row_bcast:15
+    MOE_DPP_MAX(0x143);   // row_bcast:31
 #undef MOE_DPP_MAX
     return __builtin_amdgcn_readlane(v, 63);
 }
