@@ -48,7 +48,8 @@ def _probe_weights(H, I, seed):
     return LayerWeights(g, u, d, None, None, None)
 
 
-@pytest.mark.parametrize("H,I,block_rows", [(256, 128, 32), (512, 256, 16), (2048, 512, 64)])
+@pytest.mark.parametrize("H,I,block_rows", [(256, 128, 32), (512, 256, 16), (2048, 512, 64),
+                                             (2048, 512, 32)])
 def test_one_hot_probe_bit_exact(H, I, block_rows):
     T = 96
     w = _probe_weights(H, I, seed=H + I)
@@ -85,6 +86,11 @@ SMALL = [
     (1, 2048, 512, 256, 8, 512, 32),      # batch-1 decode shape
     (9, 128, 64, 4, 4, 64, 16),           # k = E
     (50, 64, 64, 1000, 20, 64, 32),       # smallest H and I, largest E, k > 16 (radix top-k)
+    # experts of 65-200 rows at H = 512 / 1024 (64-row paired down items)
+    (301, 512, 128, 4, 2, 128, 32),       # ~150 rows per expert
+    (200, 1024, 256, 4, 4, 256, 32),      # ~200 rows per expert, two down column groups
+    (520, 512, 128, 8, 1, 0, 32),         # no shared expert, ~65 rows per expert
+    (130, 512, 256, 2, 2, 128, 32),       # I_sh < I
 ]
 
 
@@ -124,6 +130,28 @@ def test_one_expert_takes_every_token():
     assert np.all(got["routing"]["counts"][8:] == 0)
     ref = oracle_layer(w, cfg, x_bits, logits)
     assert_routing_matches(got["routing"], logits, k)
+    assert_close_layer(got["y"], ref["y"])
+
+
+def test_one_expert_takes_every_token_h512():
+    """A skewed layer at H = 512: expert 3 gets every token (330 rows: ten full 32-row
+    blocks and a ragged eleventh), the second choices spread thinly, several experts stay
+    empty."""
+    T, H, I, E, k, I_sh = 330, 512, 128, 16, 2, 128
+    cfg = small_config(T, H, I, E, k, I_sh, seed=79)
+    w = make_weights(cfg, seed=80, cache=False)
+    x_bits, logits = make_activations(cfg)
+    logits = logits.copy()
+    logits[:, 3] += np.float32(50.0)
+    logits[:, 8:] -= np.float32(50.0)
+    announce("one expert takes every token, H = 512")
+    layer = bq.MoeLayer(w, H, I, I_sh, E, k, DEV)
+    got = run_layer(layer, x_bits, logits)
+    assert int(got["routing"]["counts"][3]) == T
+    ref = oracle_layer(w, cfg, x_bits, logits)
+    assert_routing_matches(got["routing"], logits, k)
+    ok, ratio = tol_ok(bf16_bits_to_f64(got["expert_out"]), ref["expert_out"])
+    assert ok, f"expert_out {ratio:.3f}"
     assert_close_layer(got["y"], ref["y"])
 
 
