@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--only", default="", help="comma list of extra workloads to run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
     ap.add_argument("--sweep", action="store_true", help="tiling and chunking sweeps only")
+    ap.add_argument("--decode-tokens", type=int, default=1000,
+                    help="decode line over the first N of the 1000 tokens (counter runs: fewer dispatches)")
+    ap.add_argument("--no-floor", action="store_true", help="skip the decode launch-floor chains")
     return ap.parse_args()
 
 
@@ -550,7 +553,9 @@ def main():
         if not only or "decode" in only:
             c = CONFIGS["decode"]
             xd, lgd = prep(c)
-            yd = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+            n_dec = max(1, min(args.decode_tokens, c.T))
+            xd, lgd = xd[:n_dec].contiguous(), lgd[:n_dec].contiguous()
+            yd = torch.empty((n_dec, c.H), dtype=torch.bfloat16, device=dev)
             wsd = torch.empty(bq.decode_workspace_bytes(c.H, c.I, c.I_sh, c.E, c.k),
                               dtype=torch.uint8, device=dev)
             # 1000 single-token launches enqueued back to back from C, one per token
@@ -558,23 +563,24 @@ def main():
                                                       *layer.weight_mats(), yd, wsd)
             settle(seq, torch)
             msd = timed(seq, 3, 1, torch)
-            t_tok = msd * 1e-3 / c.T
+            t_tok = msd * 1e-3 / n_dec
             by_tok = 9 * expert_bytes + c.H * 4 + c.E * 4
             # the three-call path at T = 1 over the first 100 tokens, for comparison
-            xs = [xd[i:i + 1] for i in range(100)]
-            ls = [lgd[i:i + 1] for i in range(100)]
+            n3 = min(100, n_dec)
+            xs = [xd[i:i + 1] for i in range(n3)]
+            ls = [lgd[i:i + 1] for i in range(n3)]
 
             def run_tokens():
-                for i in range(100):
+                for i in range(n3):
                     layer.forward(xs[i], ls[i])
 
-            t_three = timed(run_tokens, 2, 1, torch) * 1e-3 / 100
+            t_three = timed(run_tokens, 2, 1, torch) * 1e-3 / n3
 
             # cold: token t on layer copy t mod 4.  The 1000 single-token calls are
             # captured once into a graph (no memset nodes) so the host does not pace
             # them; each replay is checked bit for bit against the same calls run eagerly.
             def decode_calls(y_out):
-                for t in range(c.T):
+                for t in range(n_dec):
                     L = layers[t % len(layers)]
                     bq.moe_decode_q4(xd[t:t + 1], lgd[t:t + 1], c.I, c.I_sh, c.k, L.block_rows,
                                      *L.weight_mats(), None, y_out[t:t + 1], wsd)
@@ -593,24 +599,38 @@ def main():
                 torch.cuda.synchronize()
                 graph_ok &= bool(torch.equal(y_graph.view(torch.int16), y_eager.view(torch.int16)))
             settle(graph.replay, torch)
-            t_cold = timed(graph.replay, 3, 1, torch) * 1e-3 / c.T
+            t_cold = timed(graph.replay, 3, 1, torch) * 1e-3 / n_dec
             del graph
             # the floor under per-token launches: the same chain of 2 launches per token with
             # the decode kernels' grid shapes, empty, then with one dependent read each
             pb = torch.zeros(3, dtype=torch.int32, device=dev)
             shapes = decode_launch_shapes(c)
-            floor = {}
-            for dep in (False, True):
-                run = lambda: bq.moe_launch_probe(pb, 2 * c.T, *shapes, dep)  # noqa: E731
+            floor = {False: float("nan"), True: float("nan")}
+            gfloor = {False: float("nan"), True: float("nan")}
+            for dep in (() if args.no_floor else (False, True)):
+                run = lambda: bq.moe_launch_probe(pb, 2 * n_dec, *shapes, dep)  # noqa: E731
                 settle(run, torch, ms=50.0)
-                floor[dep] = timed(run, 3, 1, torch) * 1e-3 / c.T
+                floor[dep] = timed(run, 3, 1, torch) * 1e-3 / n_dec
+                # the same chain replayed from a graph: no host enqueue cost, the GPU's own floor
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    run()
+                settle(g.replay, torch, ms=50.0)
+                gfloor[dep] = timed(g.replay, 3, 1, torch) * 1e-3 / n_dec
+                del g
             extra_floor = {"empty_us_per_token": floor[False] * 1e6,
                            "dependent_us_per_token": floor[True] * 1e6,
+                           "graph_empty_us_per_token": gfloor[False] * 1e6,
+                           "graph_dependent_us_per_token": gfloor[True] * 1e6,
                            "launch_shapes": shapes,
                            "what": "2 launches per token with the decode kernels' grids: empty, "
-                                   "then each reading the word the previous launch wrote"}
-            log(f"decode floor: {floor[False]*1e6:.2f} us/token empty launches, "
-                f"{floor[True]*1e6:.2f} with one dependent read per launch")
+                                   "then each reading the word the previous launch wrote; eager "
+                                   "(host enqueue rate) and replayed from a captured graph (the "
+                                   "GPU's kernel-boundary floor)"}
+            log(f"decode floor: eager {floor[False]*1e6:.2f} / {floor[True]*1e6:.2f} us/token, "
+                f"graph {gfloor[False]*1e6:.2f} / {gfloor[True]*1e6:.2f} us/token "
+                f"(empty / one dependent read per launch)")
             extra["decode"] = {"tokens_per_s": 1.0 / t_tok, "us_per_token": t_tok * 1e6,
                                "launch_floor": extra_floor,
                                "hbm_frac": by_tok / t_tok / HBM_PEAK,
@@ -621,8 +641,10 @@ def main():
                                "cold_us_per_token": t_cold * 1e6,
                                "cold_hbm_frac": by_tok / t_cold / HBM_PEAK,
                                "cold_graph_matches_eager": graph_ok,
-                               "note": "warm: 1000 single-token calls back to back on one layer; "
-                                       "cold: token t on layer copy t mod 4, replayed from a graph"}
+                               "tokens": n_dec,
+                               "note": f"warm: {n_dec} single-token calls back to back on one "
+                                       "layer; cold: token t on layer copy t mod 4, replayed from "
+                                       "a graph"}
             log(f"decode: {t_tok*1e6:.2f} us/token, HBM {100*by_tok/t_tok/HBM_PEAK:.1f}%; "
                 f"cold {t_cold*1e6:.2f} us/token (graph == eager: {graph_ok}); "
                 f"three-call path {t_three*1e6:.1f} us/token")
