@@ -342,6 +342,17 @@ def main():
         xb, lg = make_activations(c)
         return bq.bf16_from_bits(xb, dev), torch.from_numpy(lg).to(dev)
 
+    def gateup_alone_us(L, c, xx, lgx, steps):
+        """Mean duration of the gate/up call alone, back to back on the routing of one
+        layer call over (xx, lgx) (events on the launch stream)."""
+        L.forward(xx, lgx)
+        b = L.buffers(c.T)
+        fn = lambda: bq.moe_expert_gateup_q4(xx, c.I, c.I_sh, c.E, c.k, L.block_rows,  # noqa: E731
+                                             b["routing"], L.gate, L.up, L.sh_gate, L.sh_up,
+                                             b["gemm_ws"])
+        settle(fn, torch)
+        return timed(fn, steps, 5, torch) * 1e3
+
     # ---------------- headline: prefill 512 ----------------
     x, lg = prep(cfg)
     T = cfg.T
@@ -541,14 +552,19 @@ def main():
             fl = layer_flops(c.T, c.H, c.I, c.k, c.I_sh)
             by = (tch + 1) * expert_bytes + c.T * c.H * 4 + c.T * c.E * 4
             t = ms2 * 1e-3
+            gu = gateup_alone_us(layer, c, x2, lg2, max(10, args.steps // 4))
+            fl_gu = fl * 2 / 3     # gate and up: two of the three matrices
             extra["prefill2048"] = {"tokens_per_s": c.T / t, "us_per_call": ms2 * 1e3,
                                     "mfma_frac": fl / t / MFMA_BF16_PEAK,
                                     "hbm_frac": by / t / HBM_PEAK,
                                     "roofline_frac": max(fl / MFMA_BF16_PEAK, by / HBM_PEAK) / t,
                                     "cold_tokens_per_s": c.T / (ms2c * 1e-3),
-                                    "cold_us_per_call": ms2c * 1e3}
+                                    "cold_us_per_call": ms2c * 1e3,
+                                    "gateup_alone_us": gu,
+                                    "gateup_alone_mfma_frac": fl_gu / (gu * 1e-6) / MFMA_BF16_PEAK}
             log(f"prefill2048: {ms2*1e3:.1f} us/call, {c.T/t:,.0f} tok/s, "
-                f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%; cold {ms2c*1e3:.1f} us/call")
+                f"MFMA {100*fl/t/MFMA_BF16_PEAK:.1f}%; cold {ms2c*1e3:.1f} us/call; gate/up alone "
+                f"{gu:.1f} us (MFMA {100*fl_gu/(gu*1e-6)/MFMA_BF16_PEAK:.1f}%)")
             del x2, lg2
         if not only or "decode" in only:
             c = CONFIGS["decode"]
