@@ -635,18 +635,45 @@ def main():
                 settle(g.replay, torch, ms=50.0)
                 gfloor[dep] = timed(g.replay, 3, 1, torch) * 1e-3 / n_dec
                 del g
+            # a graph with an explicit parallel branch: per token, a shared-expert-sized launch
+            # S on a second stream beside launch A, joined before launch B (dependent reads)
+            gbranch = float("nan")
+            if not args.no_floor:
+                s_side = torch.cuda.Stream(device=dev)
+                s_main = torch.cuda.current_stream(dev)
+                sh_shape = [max(1, c.I_sh // 8), 256]
+
+                def branch_tokens():
+                    for _ in range(n_dec):
+                        s_side.wait_stream(s_main)
+                        bq.moe_launch_probe(pb, 1, sh_shape, sh_shape, True, stream=s_side)
+                        bq.moe_launch_probe(pb, 1, shapes[0], shapes[0], True)
+                        s_main.wait_stream(s_side)
+                        bq.moe_launch_probe(pb, 1, shapes[1], shapes[1], True)
+
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    branch_tokens()
+                settle(g.replay, torch, ms=50.0)
+                gbranch = timed(g.replay, 3, 1, torch) * 1e-3 / n_dec
+                del g
             extra_floor = {"empty_us_per_token": floor[False] * 1e6,
                            "dependent_us_per_token": floor[True] * 1e6,
                            "graph_empty_us_per_token": gfloor[False] * 1e6,
                            "graph_dependent_us_per_token": gfloor[True] * 1e6,
+                           "graph_branch_us_per_token": gbranch * 1e6,
                            "launch_shapes": shapes,
                            "what": "2 launches per token with the decode kernels' grids: empty, "
                                    "then each reading the word the previous launch wrote; eager "
                                    "(host enqueue rate) and replayed from a captured graph (the "
-                                   "GPU's kernel-boundary floor)"}
+                                   "GPU's kernel-boundary floor); graph_branch: the dependent "
+                                   "chain with a shared-expert-sized launch on a parallel graph "
+                                   "branch beside the first launch, joined before the second"}
             log(f"decode floor: eager {floor[False]*1e6:.2f} / {floor[True]*1e6:.2f} us/token, "
                 f"graph {gfloor[False]*1e6:.2f} / {gfloor[True]*1e6:.2f} us/token "
-                f"(empty / one dependent read per launch)")
+                f"(empty / one dependent read per launch); graph with a parallel branch "
+                f"{gbranch*1e6:.2f} us/token")
             extra["decode"] = {"tokens_per_s": 1.0 / t_tok, "us_per_token": t_tok * 1e6,
                                "launch_floor": extra_floor,
                                "hbm_frac": by_tok / t_tok / HBM_PEAK,
