@@ -91,6 +91,10 @@ SMALL = [
     (200, 1024, 256, 4, 4, 256, 32),      # ~200 rows per expert, two down column groups
     (520, 512, 128, 8, 1, 0, 32),         # no shared expert, ~65 rows per expert
     (130, 512, 256, 2, 2, 128, 32),       # I_sh < I
+    # large hidden sizes: gate/up scale tables of 36 and 81 KB of LDS per workgroup
+    (96, 4096, 256, 8, 2, 256, 32),
+    (96, 7168, 256, 8, 2, 256, 32),
+    (70, 7168, 2048, 4, 2, 0, 32),        # down K = 2048: the K-chunked down kernel
 ]
 
 
@@ -256,6 +260,8 @@ def test_fused_decode_sequential_equals_single(big_layer):
     (4096, 64, 8, 2, 64),        # H > 2048: several K passes per gate/up row
     (128, 128, 256, 64, 128),    # the largest k
     (64, 64, 1000, 20, 64),      # the largest E (16 logits per lane), k > 16, smallest H and I
+    (7168, 256, 8, 2, 256),      # large H
+    (7168, 2048, 4, 2, 0),       # large H and I, no shared expert
 ])
 def test_fused_decode_small_shapes(H, I, E, k, I_sh):
     cfg = small_config(6, H, I, E, k, I_sh, seed=E + k)
