@@ -274,3 +274,36 @@ def test_fused_decode_small_shapes(H, I, E, k, I_sh):
         ref = oracle_layer(w, cfg, x_bits[t:t + 1], logits[t:t + 1])
         assert_routing_matches(r, logits[t:t + 1], k)
         assert_close_layer(y, ref["y"])
+
+
+# ---------------------------------------------------------------------------
+# Property-based layer cases (hypothesis, derandomized: every run draws the same
+# examples): random shapes within the ABI's rules, both code layouts, every block
+# height; routing bit-exact and every output element within the tolerance.
+# ---------------------------------------------------------------------------
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=24, deadline=None, derandomize=True, database=None,
+          suppress_health_check=list(HealthCheck))
+@given(T=st.integers(1, 260), h64=st.integers(1, 16), i64=st.integers(1, 8),
+       E=st.integers(1, 48), kq=st.floats(0.0, 1.0), sh64=st.integers(0, 6),
+       br=st.sampled_from([16, 32, 64]), tiles=st.booleans(), seed=st.integers(0, 2 ** 20))
+def test_layer_property_random_shapes(T, h64, i64, E, kq, sh64, br, tiles, seed):
+    H, I, I_sh = 64 * h64, 64 * i64, 64 * sh64
+    k = 1 + int(kq * (min(E, 10) - 1))
+    cfg = small_config(T, H, I, E, k, I_sh, seed=seed)
+    w = make_weights(cfg, seed=seed + 1, cache=False)
+    x_bits, logits = make_activations(cfg)
+    announce(f"layer property T={T} H={H} I={I} E={E} k={k} I_sh={I_sh} br={br} "
+             f"tiles={tiles} seed={seed}")
+    layer = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=br, prepack=tiles)
+    got = run_layer(layer, x_bits, logits)
+    ref = oracle_layer(w, cfg, x_bits, logits, br)
+    assert_routing_matches(got["routing"], logits, k, br)
+    ok, ratio = tol_ok(bf16_bits_to_f64(got["expert_out"]), ref["expert_out"])
+    assert ok, f"expert_out {ratio:.3f}"
+    if I_sh:
+        ok, ratio = tol_ok(bf16_bits_to_f64(got["shared_out"]), ref["shared_out"])
+        assert ok, f"shared_out {ratio:.3f}"
+    assert_close_layer(got["y"], ref["y"])
