@@ -343,7 +343,6 @@ DecodeWs decode_ws_layout(int H, int I, int I_sh, int k) {
     w.h = take((size_t)(k + 1) * ldh * sizeof(uint16_t));
     w.sel_idx = take(kDecMaxK * sizeof(int32_t));
     w.sel_w = take(kDecMaxK * sizeof(float));
-    w.part = 0;
     w.total = o;
     return w;
 }

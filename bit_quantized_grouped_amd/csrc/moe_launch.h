@@ -75,7 +75,7 @@ struct DecodeArgs {
 };
 // Workspace offsets (bytes) and size of one decode call.
 struct DecodeWs {
-    size_t h, sel_idx, sel_w, part, total;   // part: unused (0)
+    size_t h, sel_idx, sel_w, total;
 };
 DecodeWs decode_ws_layout(int H, int I, int I_sh, int k);
 // (grid, threads) of the two decode launches.
