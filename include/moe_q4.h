@@ -35,8 +35,10 @@
  *     hipGetLastError) after earlier kernels of the same call were enqueued.
  *     Those kernels then run; the call's outputs are undefined and the
  *     caller should treat the stream as failed.
- *   - The library holds no mutable global state: calls on different streams
- *     may run concurrently from different threads if their buffers differ.
+ *   - The library holds no mutable global state except the scratch array of
+ *     moe_decode_q4_noalloc (one per device, see there): other calls on
+ *     different streams may run concurrently from different threads if their
+ *     buffers differ.
  *   - Shapes: 1 <= k <= E <= 1000; H, I, I_sh are multiples of 64 (I_sh = 0
  *     means no shared expert); T >= 1; T*k*max(H, I) < 2^30 and
  *     T*max(H, I_sh) < 2^30 (bf16 byte offsets of x, h and the outputs fit
