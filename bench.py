@@ -74,9 +74,10 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="wall time of back-to-back calls before each timed line (clock ramp)")
     ap.add_argument("--block-rows", type=int, default=32)
-    ap.add_argument("--layout", choices=("tiles", "rows"), default="tiles",
-                    help="code-word layout of the timed layer: tile-packed (load-time "
-                         "moe_q4_prepack) or row-major")
+    ap.add_argument("--layout", choices=("tiles", "tiles-codes", "rows"), default="tiles",
+                    help="weight layout of the timed layer, made at load time: tile-packed code "
+                         "words with packed gate/up scale|bias words (moe_q4_prepack, "
+                         "moe_q4_pack_scales), tile-packed code words only, or row-major")
     ap.add_argument("--other-layout", action="store_true",
                     help="also time prefill512 with the other code-word layout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -204,6 +205,17 @@ def host_grouping(idx, E, block_rows, max_blocks):
                 n_blocks=np.array([be.size], np.int32))
 
 
+def cold_copy_mats(bq, mats, i):
+    """Layer copy i for the cold runs: every code word XOR-ed with a per-copy constant,
+    scale arrays copied (same shapes, layout and routing; distinct weight bytes)."""
+    def one(m):
+        clone = lambda t: None if t is None else t.clone()  # noqa: E731
+        plain = None if m.plain is None else tuple(clone(t) for t in m.plain)
+        return bq.DeviceQMat(m.codes ^ (0x01010101 * i), clone(m.scales), clone(m.biases),
+                             m.layout, plain=plain)
+    return [None if m is None else one(m) for m in mats]
+
+
 def sweep(args, torch, bq, dev):
     from workload import CONFIGS, make_activations, make_weights
     cfg = CONFIGS["prefill512"]
@@ -211,7 +223,8 @@ def sweep(args, torch, bq, dev):
     base = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, prepack=True)
     mats = base.weight_mats()
     out = {"sweep": "block_rows x prefill, chunk_tokens x skewed prefill", "unit": "tokens/s",
-           "code_layout": "tile-packed", "warmup": args.warmup, "block_rows": {},
+           "weight_layout": "tile-packed codes, packed gate/up scale|bias words",
+           "warmup": args.warmup, "block_rows": {},
            "chunk_tokens": {}}
     for name in ("prefill512", "prefill2048"):
         c = CONFIGS[name]
@@ -316,19 +329,16 @@ def main():
                              block_rows=args.block_rows)
     # load time, outside every timed region: the same weights with tile-packed code words
     layer_tiles = bq.MoeLayer.from_device(
-        [None if m is None else m.prepacked() for m in layer_rows.weight_mats()],
+        bq.prepacked_mats(layer_rows.weight_mats(), pack_scales=args.layout != "tiles-codes"),
         cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
     torch.cuda.synchronize()
-    layer, other = ((layer_tiles, layer_rows) if args.layout == "tiles"
-                    else (layer_rows, layer_tiles))
+    layer, other = ((layer_rows, layer_tiles) if args.layout == "rows"
+                    else (layer_tiles, layer_rows))
     log(f"weights resident (timed layout: {args.layout})")
     br = layer.block_rows
-    mats0 = layer.weight_mats()
     layers = [layer] + [
-        bq.MoeLayer.from_device(
-            [None if m is None else bq.DeviceQMat(m.codes ^ (0x01010101 * i), m.scales.clone(),
-                                                  m.biases.clone(), m.layout) for m in mats0],
-            cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, dev, block_rows=args.block_rows)
+        bq.MoeLayer.from_device(cold_copy_mats(bq, layer.weight_mats(), i), cfg.H, cfg.I, cfg.I_sh,
+                                cfg.E, cfg.k, dev, block_rows=args.block_rows)
         for i in range(1, 4)]
     log("4 layer copies resident (cold runs)")
 
@@ -441,8 +451,12 @@ def main():
         "config": {"workload": "prefill512", "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "I_shared": cfg.I_sh, "block_rows": br,
                    "weights": "4-bit codes, bf16 scale+bias per 64 along K",
-                   "code_layout": "tile-packed at load time (moe_q4_prepack)" if args.layout == "tiles"
-                                  else "row-major"},
+                   "weight_layout": {
+                       "tiles": "made at load time: tile-packed code words (moe_q4_prepack), gate/up "
+                                "scale|bias words packed per 64-row tile and group "
+                                "(moe_q4_pack_scales)",
+                       "tiles-codes": "tile-packed code words at load time (moe_q4_prepack)",
+                       "rows": "row-major"}[args.layout]},
         "roofline": {"bound": "hbm", "kernel": "grouped_q4_kernel gate/up+SwiGLU (moe_expert_gateup_q4)",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": read_traffic(),
@@ -470,7 +484,7 @@ def main():
 
     # ---------------- the other code-word layout, same weights ----------------
     if args.other_layout:
-        other_name = "rows" if args.layout == "tiles" else "tiles"
+        other_name = "tiles" if args.layout == "rows" else "rows"
         ms_ot = timed(lambda: other.forward(x, lg), args.steps, args.warmup, torch)
         result["layer"][f"{other_name}_layout_us_per_call"] = ms_ot * 1e3
         result["layer"][f"{other_name}_layout_tokens_per_s"] = T / (ms_ot * 1e-3)
@@ -597,7 +611,7 @@ def main():
                               dtype=torch.uint8, device=dev)
             # 1000 single-token launches enqueued back to back from C, one per token
             seq = lambda: bq.moe_decode_q4_sequential(xd, lgd, c.I, c.I_sh, c.k,
-                                                      *layer.weight_mats(), yd, wsd)
+                                                      *layer.decode_mats(), yd, wsd)
             settle(seq, torch)
             msd = timed(seq, 3, 1, torch)
             t_tok = msd * 1e-3 / n_dec
@@ -620,7 +634,7 @@ def main():
                 for t in range(n_dec):
                     L = layers[t % len(layers)]
                     bq.moe_decode_q4(xd[t:t + 1], lgd[t:t + 1], c.I, c.I_sh, c.k, L.block_rows,
-                                     *L.weight_mats(), None, y_out[t:t + 1], wsd)
+                                     *L.decode_mats(), None, y_out[t:t + 1], wsd)
             y_eager = torch.empty_like(yd)
             decode_calls(y_eager)
             y_graph = torch.zeros_like(yd)

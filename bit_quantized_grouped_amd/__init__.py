@@ -33,6 +33,7 @@ class MoeError(RuntimeError):
 
 LAYOUT_ROWS = 0      # row-major code words
 LAYOUT_TILES = 1     # tile-packed code words (moe_q4_prepack)
+LAYOUT_TILES_SB = 2  # tile-packed code words + packed scale|bias words (moe_q4_pack_scales)
 
 
 class MoeQ4Mat(ctypes.Structure):
@@ -69,6 +70,7 @@ _SIGNATURES = {
     "moe_combine": (_I, [_P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
     "moe_dequant_q4_bf16": (_I, [ctypes.POINTER(MoeQ4Mat), _I, _I, _I, _P, _P, _P]),
     "moe_q4_prepack": (_I, [_P, _I, _I, _I, _P, _P]),
+    "moe_q4_pack_scales": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "moe_combine_gated": (_I, [_P, _P, _P, ctypes.POINTER(MoeRouting), _I, _I, _I, _P, _P]),
     "moe_router": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P]),
     "moe_expert_gateup_bf16": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting)]
@@ -188,12 +190,16 @@ def _qmat_for(m, name, n_exp, N, K, present=True):
         return None
     if not isinstance(m, DeviceQMat):
         raise TypeError(f"{name}: expected a DeviceQMat")
-    if K % 64 or (m.codes.shape, m.scales.shape, m.biases.shape) != (
-            (n_exp, N, K // 8), (n_exp, N, K // 64), (n_exp, N, K // 64)):
+    packed = m.layout == LAYOUT_TILES_SB
+    b_shape = None if m.biases is None else tuple(m.biases.shape)
+    if K % 64 or (tuple(m.codes.shape), tuple(m.scales.shape), b_shape) != (
+            (n_exp, N, K // 8), (n_exp, N, K // 64), None if packed else (n_exp, N, K // 64)):
         raise ValueError(f"{name}: codes {tuple(m.codes.shape)}, scales {tuple(m.scales.shape)}, "
-                         f"biases {tuple(m.biases.shape)} do not hold a [{n_exp}, {N}, {K}] set")
+                         f"biases {b_shape} do not hold a [{n_exp}, {N}, {K}] set"
+                         + (" with packed scale|bias words" if packed else ""))
     for part in ("codes", "scales", "biases"):
-        _tensor(getattr(m, part), f"{name}.{part}")
+        if getattr(m, part) is not None:
+            _tensor(getattr(m, part), f"{name}.{part}")
     return m
 
 
@@ -223,20 +229,40 @@ def _stream(stream, device):
 class DeviceQMat:
     """One 4-bit matrix set [n_exp, N, K] resident on the device."""
 
-    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
-                 layout: int = LAYOUT_ROWS):
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, biases,
+                 layout: int = LAYOUT_ROWS, plain=None):
+        """layout LAYOUT_TILES_SB: scales holds the packed scale|bias words (int32, same
+        shape as the bf16 scales) and biases is None; plain optionally keeps the bf16
+        (scales, biases) they were packed from, for the row-wise readers (decode)."""
         self.codes, self.scales, self.biases, self.layout = codes, scales, biases, layout
-        self.struct = MoeQ4Mat(codes.data_ptr(), scales.data_ptr(), biases.data_ptr(), layout)
+        self.plain = plain
+        self.struct = MoeQ4Mat(codes.data_ptr(), scales.data_ptr(),
+                               None if biases is None else biases.data_ptr(), layout)
 
-    def prepacked(self, stream=None) -> "DeviceQMat":
-        """The same matrices with the code words in the tile-packed order (scales and biases
-        are shared with this object)."""
+    def row_view(self) -> "DeviceQMat":
+        """The matrices for calls that read scales row by row (batch-1 decode): a
+        LAYOUT_TILES view over the same code words and the plain scales, when this
+        object has packed scale|bias words and kept the plain ones; else itself."""
+        if self.layout == LAYOUT_TILES_SB and self.plain is not None:
+            return DeviceQMat(self.codes, self.plain[0], self.plain[1], LAYOUT_TILES)
+        return self
+
+    def prepacked(self, pack_scales: bool = False, stream=None) -> "DeviceQMat":
+        """The same matrices with the code words in the tile-packed order (load time); with
+        pack_scales also the scales and biases packed into scale|bias words
+        (LAYOUT_TILES_SB), else shared with this object (LAYOUT_TILES)."""
         assert self.layout == LAYOUT_ROWS
         n_exp, N, G = self.scales.shape
         dst = torch.empty_like(self.codes)
-        _check(lib().moe_q4_prepack(_ptr(self.codes), n_exp, N, G * 64, _ptr(dst),
-                                    _stream(stream, dst.device)), "moe_q4_prepack")
-        return DeviceQMat(dst, self.scales, self.biases, LAYOUT_TILES)
+        st = _stream(stream, dst.device)
+        _check(lib().moe_q4_prepack(_ptr(self.codes), n_exp, N, G * 64, _ptr(dst), st),
+               "moe_q4_prepack")
+        if not pack_scales:
+            return DeviceQMat(dst, self.scales, self.biases, LAYOUT_TILES)
+        sb = torch.empty((n_exp, N, G), dtype=torch.int32, device=dst.device)
+        _check(lib().moe_q4_pack_scales(_ptr(self.scales), _ptr(self.biases), n_exp, N, G * 64,
+                                        _ptr(sb), st), "moe_q4_pack_scales")
+        return DeviceQMat(dst, sb, None, LAYOUT_TILES_SB, plain=(self.scales, self.biases))
 
     @classmethod
     def from_host(cls, m, device) -> "DeviceQMat":
@@ -248,7 +274,17 @@ class DeviceQMat:
 
     @property
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.biases))
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.biases)
+                   if t is not None)
+
+
+def prepacked_mats(mats, pack_scales: bool = True, stream=None):
+    """Load time: a layer's six row-major matrix sets (gate, up, down, sh_gate, sh_up,
+    sh_down; None skipped) with tile-packed code words, and with pack_scales the gate and
+    up sets' scales and biases packed too (LAYOUT_TILES_SB; the down sets stay
+    LAYOUT_TILES)."""
+    return tuple(None if m is None else m.prepacked(pack_scales and i in (0, 1, 3, 4), stream)
+                 for i, m in enumerate(mats))
 
 
 class DeviceRouting:
@@ -619,7 +655,9 @@ class MoeLayer:
     """Device-resident weights of one layer plus per-call buffers for T tokens."""
 
     def __init__(self, weights, H: int, I: int, I_sh: int, E: int, k: int, device,
-                 block_rows: int = 32, prepack: bool = False):
+                 block_rows: int = 32, prepack=False):
+        """prepack: False (row-major code words), True (tile-packed code words, packed
+        gate/up scale|bias words) or "codes" (tile-packed code words only)."""
         self.H, self.I, self.I_sh, self.E, self.k = H, I, I_sh, E, k
         self.block_rows = block_rows
         self.device = torch.device(device)
@@ -627,11 +665,10 @@ class MoeLayer:
         self.gate, self.up, self.down = up(weights.gate), up(weights.up), up(weights.down)
         self.sh_gate, self.sh_up, self.sh_down = (up(weights.sh_gate), up(weights.sh_up),
                                                   up(weights.sh_down))
-        if prepack:   # load time: code words into the tile-packed order, row-major copies freed
-            for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
-                m = getattr(self, name)
-                if m is not None:
-                    setattr(self, name, m.prepacked())
+        if prepack:   # load time: tile-packed code words and, unless prepack == "codes", packed
+            # gate/up scale|bias words; the row-major copies are freed
+            (self.gate, self.up, self.down, self.sh_gate, self.sh_up,
+             self.sh_down) = prepacked_mats(self.weight_mats(), pack_scales=prepack != "codes")
             torch.cuda.synchronize(self.device)
         self._bufs = {}
 
@@ -650,6 +687,11 @@ class MoeLayer:
 
     def weight_mats(self):
         return (self.gate, self.up, self.down, self.sh_gate, self.sh_up, self.sh_down)
+
+    def decode_mats(self):
+        """The six matrix sets for batch-1 decode, which reads scales row by row: packed
+        scale|bias sets are given as their plain-scale views (same code words)."""
+        return tuple(None if m is None else m.row_view() for m in self.weight_mats())
 
     def buffers(self, T: int) -> dict:
         if T not in self._bufs:
@@ -698,7 +740,7 @@ class MoeLayer:
         if ws is None:
             ws = _bytes_tensor(decode_workspace_bytes(self.H, self.I, self.I_sh, self.E, self.k),
                                self.device)
-        moe_decode_q4(x, logits, self.I, self.I_sh, self.k, self.block_rows, *self.weight_mats(),
+        moe_decode_q4(x, logits, self.I, self.I_sh, self.k, self.block_rows, *self.decode_mats(),
                       routing, y, ws, stream)
         return ws
 

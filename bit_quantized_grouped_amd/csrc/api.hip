@@ -14,7 +14,7 @@ using namespace moeq4;
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kMaxE = 1000;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -42,7 +42,12 @@ int check_layer_shape(int T, int H, int I, int I_sh, int E, int k, int block_row
 }
 
 int check_mat(const moe_q4_mat* m) {
-    if (!m || !m->codes || !m->scales || !m->biases) return MOE_ERR_NULL;
+    if (!m || !m->codes || !m->scales) return MOE_ERR_NULL;
+    if (m->layout == MOE_Q4_LAYOUT_TILES_SB) {   // packed scale|bias words; biases not read
+        if (!aligned(m->codes, 16) || !aligned(m->scales, 4)) return MOE_ERR_ALIGN;
+        return MOE_OK;
+    }
+    if (!m->biases) return MOE_ERR_NULL;
     if (!aligned(m->codes, 16) || !aligned(m->scales, 2) || !aligned(m->biases, 2))
         return MOE_ERR_ALIGN;
     if (m->layout != MOE_Q4_LAYOUT_ROWS && m->layout != MOE_Q4_LAYOUT_TILES) return MOE_ERR_SHAPE;
@@ -57,6 +62,29 @@ static int check_same_layout(std::initializer_list<const moe_q4_mat*> mats) {
         if (layout < 0) layout = m->layout;
         else if (m->layout != layout) return MOE_ERR_SHAPE;
     }
+    return MOE_OK;
+}
+
+static int code_order(const moe_q4_mat* m) {
+    return m->layout == MOE_Q4_LAYOUT_ROWS ? MOE_Q4_LAYOUT_ROWS : MOE_Q4_LAYOUT_TILES;
+}
+
+// The layout rules of one layer's matrices (NULL ones skipped): gate, up, sh_gate and sh_up
+// share one layout; down and sh_down share one, which is not TILES_SB; all share one
+// code-word order.
+static int check_layer_layouts(const moe_q4_mat* gate, const moe_q4_mat* up,
+                               const moe_q4_mat* down, const moe_q4_mat* sh_gate,
+                               const moe_q4_mat* sh_up, const moe_q4_mat* sh_down) {
+    int st = check_same_layout({gate, up, sh_gate, sh_up});
+    if (st || (st = check_same_layout({down, sh_down}))) return st;
+    int order = -1;
+    for (const moe_q4_mat* m : {gate, up, down, sh_gate, sh_up, sh_down}) {
+        if (!m) continue;
+        if (order < 0) order = code_order(m);
+        else if (code_order(m) != order) return MOE_ERR_SHAPE;
+    }
+    for (const moe_q4_mat* m : {down, sh_down})
+        if (m && m->layout == MOE_Q4_LAYOUT_TILES_SB) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -137,7 +165,7 @@ int gemm_args_ok(const uint16_t* x, int T, int H, int I, int I_sh, int E, int k,
     } else if (sh_gate || sh_up || sh_down || shared_out) {
         return MOE_ERR_SHAPE;   // shared matrices given but I_sh == 0
     }
-    if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
+    if ((st = check_layer_layouts(gate, up, down, sh_gate, sh_up, sh_down))) return st;
     if (!aligned(x, 16) || !aligned(expert_out, 16)) return MOE_ERR_ALIGN;
     return MOE_OK;
 }
@@ -330,7 +358,7 @@ int moe_expert_down_q4(int T, int H, int I, int I_sh, int E, int k, int block_ro
         if (!expert_out) return MOE_ERR_NULL;
         if ((st = check_routing(r))) return st;
         if ((st = check_mat(down))) return st;
-        if ((st = check_same_layout({down, sh_down}))) return st;
+        if ((st = check_layer_layouts(nullptr, nullptr, down, nullptr, nullptr, sh_down))) return st;
         if (I_sh) {
             if (!shared_out) return MOE_ERR_NULL;
             if ((st = check_mat(sh_down))) return st;
@@ -359,6 +387,23 @@ int moe_q4_prepack(const uint32_t* src_codes, int n_exp, int N, int K, uint32_t*
         if (src_codes == dst_codes) return MOE_ERR_SHAPE;
         if (!aligned(src_codes, 16) || !aligned(dst_codes, 16)) return MOE_ERR_ALIGN;
         return launch_prepack(src_codes, n_exp, N, K, dst_codes, stream) == hipSuccess
+                   ? MOE_OK
+                   : MOE_ERR_HIP;
+    } catch (...) {
+        return MOE_ERR_HIP;
+    }
+}
+
+int moe_q4_pack_scales(const uint16_t* scales, const uint16_t* biases, int n_exp, int N, int K,
+                       uint32_t* dst, hipStream_t stream) {
+    try {
+        if (n_exp < 1 || N < 64 || N % 64 || K < 64 || K % 64) return MOE_ERR_SHAPE;
+        if ((size_t)n_exp * N * (K / 64) >= ((size_t)1 << 31)) return MOE_ERR_SHAPE;
+        if (!scales || !biases || !dst) return MOE_ERR_NULL;
+        if ((const void*)dst == (const void*)scales || (const void*)dst == (const void*)biases)
+            return MOE_ERR_SHAPE;
+        if (!aligned(scales, 2) || !aligned(biases, 2) || !aligned(dst, 4)) return MOE_ERR_ALIGN;
+        return launch_pack_scales(scales, biases, n_exp, N, K, dst, stream) == hipSuccess
                    ? MOE_OK
                    : MOE_ERR_HIP;
     } catch (...) {
@@ -561,7 +606,7 @@ int decode_args(const uint16_t* x, const float* logits, int H, int I, int I_sh, 
     } else if (sh_gate || sh_up || sh_down) {
         return MOE_ERR_SHAPE;
     }
-    if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
+    if ((st = check_layer_layouts(gate, up, down, sh_gate, sh_up, sh_down))) return st;
     if (r && (st = check_routing(r))) return st;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4)) return MOE_ERR_ALIGN;
     *a = DecodeArgs{};
@@ -720,7 +765,7 @@ int moe_layer_chunked(const uint16_t* x, const float* logits, int T, int H, int 
         } else if (sh_gate || sh_up || sh_down) {
             return MOE_ERR_SHAPE;
         }
-        if ((st = check_same_layout({gate, up, down, sh_gate, sh_up, sh_down}))) return st;
+        if ((st = check_layer_layouts(gate, up, down, sh_gate, sh_up, sh_down))) return st;
         if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, 256))
             return MOE_ERR_ALIGN;
         const LayerWs L = layer_ws_layout(C, H, I, I_sh, E, k, block_rows);

@@ -152,7 +152,9 @@ __device__ void write_routing_t1(const DecodeArgs& p, const int* s_idx, const fl
     if (tid == 0) p.r.n_blocks[0] = k;
 }
 
-template <int EPL>
+// SB: gate and up carry packed scale|bias words (MOE_Q4_LAYOUT_TILES_SB), word
+// ((row / 64) * G + group) * 64 + row % 64 of the matrix set.
+template <int EPL, bool SB>
 __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p) {
     __shared__ int s_idx[kDecMaxK];
     __shared__ float s_w[kDecMaxK];
@@ -187,6 +189,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
         const uint32_t* gc[kGuRows];   // expert's code matrix (row n_r is addressed per layout)
         const uint32_t* uc[kGuRows];
         const uint16_t *gs[kGuRows], *gb[kGuRows], *us[kGuRows], *ub[kGuRows];
+        const uint32_t *gsb[kGuRows], *usb[kGuRows];   // SB: the row's word of group 0
         int hidx[kGuRows], nrow[kGuRows];
 #pragma unroll
         for (int r = 0; r < kGuRows; ++r) {
@@ -205,6 +208,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
             gb[r] = g.biases + row * (H / 64);
             us[r] = u.scales + row * (H / 64);
             ub[r] = u.biases + row * (H / 64);
+            const size_t sbw = (row / 64) * (size_t)(H / 64) * 64 + row % 64;
+            gsb[r] = (const uint32_t*)g.scales + sbw;
+            usb[r] = (const uint32_t*)u.scales + sbw;
             hidx[r] = t0 + r < n_tasks ? j * ldh + n : -1;
         }
         float acc[2 * kGuRows];
@@ -222,10 +228,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
                 const uint32_t wo = code_word(p.gate.layout, nrow[r], kb / 8, H);
                 gw[r] = *(const u32x4_t*)(gc[r] + wo);
                 uw[r] = *(const u32x4_t*)(uc[r] + wo);
-                sg[r] = bf16_to_f32(gs[r][grp]);
-                bg[r] = bf16_to_f32(gb[r][grp]);
-                su[r] = bf16_to_f32(us[r][grp]);
-                bu[r] = bf16_to_f32(ub[r][grp]);
+                if constexpr (SB) {
+                    const uint32_t wg = gsb[r][grp * 64], wu = usb[r][grp * 64];
+                    sg[r] = bf16_to_f32((uint16_t)(wg & 0xFFFFu));
+                    bg[r] = bf16_to_f32((uint16_t)(wg >> 16));
+                    su[r] = bf16_to_f32((uint16_t)(wu & 0xFFFFu));
+                    bu[r] = bf16_to_f32((uint16_t)(wu >> 16));
+                } else {
+                    sg[r] = bf16_to_f32(gs[r][grp]);
+                    bg[r] = bf16_to_f32(gb[r][grp]);
+                    su[r] = bf16_to_f32(us[r][grp]);
+                    bu[r] = bf16_to_f32(ub[r][grp]);
+                }
             }
             // every load of the pass is issued before the first wait (the scheduler
             // would otherwise interleave them with the math, one row per round trip)
@@ -356,18 +370,23 @@ void decode_launch_shapes(int H, int I, int I_sh, int k, int* grid1, int* thread
     *threads2 = kDnThreads;
 }
 
+template <int EPL>
+static void launch_gateup_epl(const DecodeArgs& args, int g1, int t1, hipStream_t stream) {
+    if (args.gate.layout == 2)
+        hipLaunchKernelGGL((decode_gateup_kernel<EPL, true>), dim3(g1), dim3(t1), 0, stream, args);
+    else
+        hipLaunchKernelGGL((decode_gateup_kernel<EPL, false>), dim3(g1), dim3(t1), 0, stream, args);
+}
+
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
     int g1, t1, g2, t2;
     decode_launch_shapes(args.H, args.I, args.I_sh, args.k, &g1, &t1, &g2, &t2);
     const int epl = (args.E + WAVE - 1) / WAVE;
-#define MOE_DECODE_GU(N) \
-    hipLaunchKernelGGL(decode_gateup_kernel<N>, dim3(g1), dim3(t1), 0, stream, args)
-    if (epl <= 1) MOE_DECODE_GU(1);
-    else if (epl <= 2) MOE_DECODE_GU(2);
-    else if (epl <= 4) MOE_DECODE_GU(4);
-    else if (epl <= 8) MOE_DECODE_GU(8);
-    else MOE_DECODE_GU(16);
-#undef MOE_DECODE_GU
+    if (epl <= 1) launch_gateup_epl<1>(args, g1, t1, stream);
+    else if (epl <= 2) launch_gateup_epl<2>(args, g1, t1, stream);
+    else if (epl <= 4) launch_gateup_epl<4>(args, g1, t1, stream);
+    else if (epl <= 8) launch_gateup_epl<8>(args, g1, t1, stream);
+    else launch_gateup_epl<16>(args, g1, t1, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_down_kernel, dim3(g2), dim3(t2), 0, stream, args);

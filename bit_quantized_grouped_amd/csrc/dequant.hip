@@ -1,5 +1,6 @@
 // Weight-format utilities: the load-time repack of code words into the
-// tile-packed order, and the expansion of 4-bit groupwise-affine weights
+// tile-packed order and of scales and biases into packed scale|bias words,
+// and the expansion of 4-bit groupwise-affine weights
 // into a bf16 matrix in memory, the unfused layout that the pages measure
 // the fused grouped GEMM against
 // ([P2] aikraft.ru, "Technical optimizations: Prefill and Decode"; [P3]
@@ -45,6 +46,27 @@ __global__ __launch_bounds__(kDqThreads) void prepack_kernel(const uint32_t* __r
     const uint32_t e = row / N, n = row % N;
     const size_t to = (size_t)e * N * words_per_row + code_word(1, n, c, K);
     *(u32x4_t*)(dst + to) = *(const u32x4_t*)(src + w);
+}
+
+// Scales and biases into the packed scale|bias order (moe_q4_pack_scales,
+// load time): thread i writes word i of the packed array, i = ((n/64)*G +
+// g)*64 + n%64 for global row n and group g, so the stores are coalesced.
+__global__ __launch_bounds__(kDqThreads) void pack_scales_kernel(
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t G,
+    uint32_t total, uint32_t* __restrict__ dst) {
+    const uint32_t i = blockIdx.x * kDqThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t r = i % 64, g = (i / 64) % G, tile = i / (64 * G);
+    const uint32_t src = (tile * 64 + r) * G + g;
+    dst[i] = (uint32_t)scales[src] | ((uint32_t)biases[src] << 16);
+}
+
+hipError_t launch_pack_scales(const uint16_t* scales, const uint16_t* biases, int n_exp, int N,
+                              int K, uint32_t* dst, hipStream_t stream) {
+    const uint32_t total = (uint32_t)((size_t)n_exp * N * (K / 64));
+    pack_scales_kernel<<<(total + kDqThreads - 1) / kDqThreads, kDqThreads, 0, stream>>>(
+        scales, biases, (uint32_t)(K / 64), total, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_prepack(const uint32_t* src, int n_exp, int N, int K, uint32_t* dst,

@@ -45,6 +45,11 @@
 #ifndef MOE_GU_DEPTH
 #define MOE_GU_DEPTH 4
 #endif
+// With packed scale|bias words the workgroup needs only the A tiles in LDS;
+// a 2-deep ring then keeps the registers low enough for 6 waves per SIMD.
+#ifndef MOE_GU_SB_DEPTH
+#define MOE_GU_SB_DEPTH 2
+#endif
 #ifndef MOE_DN_WAVES
 #define MOE_DN_WAVES 8
 #endif
@@ -114,6 +119,7 @@ struct BChunk {
     u32x4_t w[NMAT][NSUB][W / 4 > 0 ? W / 4 : 1];
     u32x2_t w2[NMAT][NSUB];           // used when W == 2
     u32x4_t wb[NMAT][NSUB][BF ? W : 1];
+    uint32_t sb[NMAT][NSUB];          // packed scale|bias word of the lane's row and group (SB)
 };
 
 template <int NMAT, int NSUB, int KC>
@@ -124,6 +130,9 @@ struct Streams {
     int sub_off[NSUB];                // byte offset of subtile s (tile-packed codes)
     int chunk_c;                      // byte step per K-chunk in codes
     bool tiles;                       // codes are tile-packed
+    rsrc_t sbr[NMAT];                 // packed scale|bias words (SB)
+    int sb_off[NSUB];                 // per-lane byte offset of subtile s in them
+    int sb_chunk;                     // byte step per K-chunk in them
 };
 
 // Chunks past the last one (pipeline run-out) are requested with kVoffOob
@@ -134,7 +143,7 @@ struct Streams {
 // loads it waits for all of them once per pass over the register ring).
 constexpr int kVoffOob = 0x40000000;
 
-template <int NMAT, int NSUB, int KC, bool BF>
+template <int NMAT, int NSUB, int KC, bool BF, bool SB>
 __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                        const Streams<NMAT, NSUB, KC>& S, int c, int voff_oob) {
     constexpr int W = KC / 32;
@@ -142,6 +151,9 @@ __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32, BF>& B,
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
+            if constexpr (SB)
+                B.sb[m][s] = __builtin_amdgcn_raw_buffer_load_b32(
+                    S.sbr[m], S.sb_off[s] + voff_oob, c * S.sb_chunk, 0);
             if constexpr (BF) {   // bf16 rows: K * 2 bytes; a chunk is KC * 2 bytes of a row
                 const int so_b = s * S.sub_c + c * (KC * 2);
 #pragma unroll
@@ -174,7 +186,7 @@ __device__ __forceinline__ uint32_t word_of(const BChunk<NMAT, NSUB, W, BF>& B, 
 
 // sSc / sBi: this lane's row of bf16 scales / biases in LDS (row stride GS,
 // matrix stride mstride); grp = the group of the lane's words in this chunk.
-template <int NMAT, int MT, int KC, int NSUB, bool BF>
+template <int NMAT, int MT, int KC, int NSUB, bool BF, bool SB>
 __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                               const uint16_t* sAc, const uint16_t* sSc,
                                               const uint16_t* sBi, int GS, int mstride, int grp,
@@ -188,6 +200,11 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, 
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
             if constexpr (BF) break;
+            if constexpr (SB) {
+                sc[m][s] = bf16_to_f32((uint16_t)(B.sb[m][s] & 0xFFFFu)) * unit_inv;
+                bi[m][s] = bf16_to_f32((uint16_t)(B.sb[m][s] >> 16));
+                continue;
+            }
             const int at = m * mstride + s * 16 * GS + grp;
             sc[m][s] = bf16_to_f32(sSc[at]) * unit_inv;
             bi[m][s] = bf16_to_f32(sBi[at]);
@@ -216,7 +233,12 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, 
 
 // BF: the weights are plain bf16 [n_exp, N, K] (rW / sW), already expanded
 // in memory; the unfused layout the pages compare against.
-template <int NMAT, int MT, int KC, int NSUB, int DEPTH, int WAVES, bool BF = false>
+// SB: the matrices carry packed scale|bias words (MOE_Q4_LAYOUT_TILES_SB):
+// each lane loads its row's word for the chunk's group with its code words,
+// so the workgroup keeps no scale table in LDS and preloads nothing (the
+// LDS holds only the A tiles, which lets more workgroups share a CU).
+template <int NMAT, int MT, int KC, int NSUB, int DEPTH, int WAVES, bool BF = false,
+          bool SB = false>
 __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     constexpr int NT = WAVES * 64;   // threads
     constexpr int W = KC / 32;       // code words per lane per chunk
@@ -294,6 +316,10 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         }
         const QMatDev& q = is_sh ? p.sB[m] : p.rB[m];
         S.codes[m] = make_rsrc(q.codes + rows0 * (K / 8), (uint32_t)N * (K / 2));
+        if constexpr (SB) {   // packed words [row / 64][group][row % 64] of this expert
+            S.sbr[m] = make_rsrc((const uint32_t*)q.scales + rows0 * G, (uint32_t)N * G * 4);
+            continue;
+        }
         const rsrc_t rs_s = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
         const rsrc_t rs_b = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
         const int pieces = ROWS * G / 8;
@@ -342,6 +368,14 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         }
     }
     const int lane_grp = (g * (KC / 4)) / 64;
+    if constexpr (SB) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            const int r = n_base + row_lane + 16 * s;   // row within the expert's matrix
+            S.sb_off[s] = (((r / 64) * G + lane_grp) * 64 + r % 64) * 4;
+        }
+        S.sb_chunk = (KC / 64) * 64 * 4;
+    }
     const uint16_t* sSc_lane = sSc + row_lane * GS + lane_grp;
     const uint16_t* sBi_lane = sBi + row_lane * GS + lane_grp;
     const int mstride = ROWS * GS;
@@ -396,7 +430,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     for (int d = 0; d < DEPTH - 1; ++d) {
         const int oob = d < nchunks ? 0 : kVoffOob;
         load_a(Aq[d], d, oob);
-        load_b<NMAT, NSUB, KC>(Bq[d], S, d, oob);
+        load_b<NMAT, NSUB, KC, BF, SB>(Bq[d], S, d, oob);
     }
     store_a(Aq[0], sA);
     __syncthreads();
@@ -407,9 +441,9 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
             const int cp = c + DEPTH - 1;
             const int oob = cp < nchunks ? 0 : kVoffOob;
             load_a(Aq[(d + DEPTH - 1) % DEPTH], cp, oob);
-            load_b<NMAT, NSUB, KC>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
+            load_b<NMAT, NSUB, KC, BF, SB>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
             if (c < nchunks) {
-                compute_chunk<NMAT, MT, KC, NSUB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane,
+                compute_chunk<NMAT, MT, KC, NSUB, BF, SB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane,
                                                   sBi_lane, GS, mstride, c * KC / 64, unit_inv, nl,
                                                   g, msub_act, acc);
                 // after the last chunk this stages unused data into the idle buffer
@@ -661,12 +695,13 @@ static size_t down_tiles_lds_bytes() {
     return a > o ? a : o;
 }
 
-// Dynamic LDS bytes of one grouped_q4_kernel instance for K-groups G.
-template <int NMAT, int MT, int KC, int NSUB, int WAVES>
+// Dynamic LDS bytes of one grouped_q4_kernel instance for K-groups G (with
+// packed scale|bias words, SB, there is no scale table).
+template <int NMAT, int MT, int KC, int NSUB, int WAVES, bool SB = false>
 static size_t grouped_lds_bytes(int G, int wg_per_cu) {
     constexpr int LDA = KC + 8;
     constexpr int ROWS = WAVES * NSUB * 16;
-    const size_t a = (size_t)2 * MT * LDA * 2 + (size_t)2 * NMAT * ROWS * (G + 8) * 2;
+    const size_t a = (size_t)2 * MT * LDA * 2 + (SB ? 0 : (size_t)2 * NMAT * ROWS * (G + 8) * 2);
     const size_t o = (size_t)MT * ROWS * 2;
     size_t bytes = a > o ? a : o;
     if (wg_per_cu > 0) {
@@ -691,28 +726,29 @@ static int pick_kc(int K, int K2, int kc_max) {
     return 0;
 }
 
-template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES, bool BF>
+template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES, bool BF, bool SB>
 static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_cu,
                       hipStream_t stream) {
 #define MOE_LAUNCH(KCV)                                                                          \
-    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES, BF><<<                                  \
-        grid, WAVES * 64, grouped_lds_bytes<NMAT, MT, KCV, NSUB, WAVES>(G, wg_per_cu), stream>>>(a)
+    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES, BF, SB><<<                              \
+        grid, WAVES * 64, grouped_lds_bytes<NMAT, MT, KCV, NSUB, WAVES, SB>(G, wg_per_cu),        \
+        stream>>>(a)
     if (kc == 256) MOE_LAUNCH(256);
     else if (kc == 128) MOE_LAUNCH(128);
     else MOE_LAUNCH(64);
 #undef MOE_LAUNCH
 }
 
-template <int NMAT, int NSUB, int DEPTH, int WAVES, bool BF = false>
+template <int NMAT, int NSUB, int DEPTH, int WAVES, bool BF = false, bool SB = false>
 static void launch_grouped(GroupedArgs a, int mt, int kc, int n_max, int slots, int G,
                            int wg_per_cu, hipStream_t stream) {
     constexpr int cols = WAVES * NSUB * 16;
     a.n_tiles = (n_max + cols - 1) / cols;
     const long long items = (long long)slots * a.n_tiles;
     const int grid = (int)((items + kXcds - 1) / kXcds) * kXcds;
-    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES, BF>(a, kc, grid, G, wg_per_cu, stream);
-    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES, BF>(a, kc, grid, G, wg_per_cu, stream);
-    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES, BF>(a, kc, grid, G, wg_per_cu, stream);
+    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
+    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
+    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
 }
 
 static GroupedArgs common_args(const GemmProblem& p) {
@@ -776,6 +812,12 @@ static GroupedArgs down_args(const GemmProblem& p, const void* ws) {
 
 hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
     const GroupedArgs a = gateup_args(p, ws);
+    if (p.gate.layout == 2) {   // packed scale|bias words: no LDS table, a shorter ring
+        launch_grouped<2, MOE_GU_NSUB, MOE_GU_SB_DEPTH, MOE_GU_WAVES, false, true>(
+            a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
+            a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
+        return hipGetLastError();
+    }
     launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES>(
         a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
         a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);

@@ -14,7 +14,8 @@ struct QMatDev {
     const uint32_t* codes;
     const uint16_t* scales;
     const uint16_t* biases;
-    int layout;               // 0 = row-major code words, 1 = tile-packed (moe_q4_prepack)
+    int layout;               // 0 = row-major code words, 1 = tile-packed (moe_q4_prepack),
+                              // 2 = tile-packed with packed scale|bias words in `scales`
 };
 
 struct RoutingDev {
@@ -56,6 +57,8 @@ hipError_t launch_down_bf16(const GemmProblem& p, const uint16_t* down, const ui
 // dequant.hip
 hipError_t launch_prepack(const uint32_t* src, int n_exp, int N, int K, uint32_t* dst,
                           hipStream_t stream);
+hipError_t launch_pack_scales(const uint16_t* scales, const uint16_t* biases, int n_exp, int N,
+                              int K, uint32_t* dst, hipStream_t stream);
 hipError_t launch_dequant_bf16(const QMatDev& m, int n_exp, int N, int K, const int32_t* counts,
                                uint16_t* out, hipStream_t stream);
 

@@ -76,15 +76,29 @@ extern "C" {
  *            MOE_Q4_LAYOUT_ROWS   word (n, c) at n*(K/8) + c (row-major);
  *            MOE_Q4_LAYOUT_TILES  the tile-packed order moe_q4_prepack
  *                                 writes (see there);
+ *            MOE_Q4_LAYOUT_TILES_SB  the same tile-packed order;
  *   scales bf16   [n_exp, N, K/64]: scale of weights (n, 64g .. 64g+63);
- *   biases bf16   [n_exp, N, K/64] (row-major in both layouts).
+ *   biases bf16   [n_exp, N, K/64] (row-major in the first two layouts).
+ *   MOE_Q4_LAYOUT_TILES_SB keeps each scale and its bias together in the
+ *   order moe_q4_pack_scales writes: `scales` then points to n_exp*N*K/64
+ *   uint32 words, word ((n/64)*(K/64) + g)*64 + n%64 holding the scale's
+ *   bits in its low half and the bias's bits in its high half (n = e*N + n',
+ *   4-byte aligned), and `biases` is not read (may be NULL).  The 64 rows of
+ *   a tile then have their pairs for one group in 256 contiguous bytes, so a
+ *   grouped-GEMM chunk reads them with its code words instead of keeping a
+ *   table of the whole K in LDS.
  * Weight value: w = bf16_rne(fp32(q * scale + bias)) ([P1] "Prefill
  * optimizations"; [P3] "A big model ...").  Gate and up are [E, I, H],
  * down is [E, H, I]; the shared expert's are [1, I_sh, H] and [1, H, I_sh].
  * A zero-initialised layout is MOE_Q4_LAYOUT_ROWS.  The matrices passed to
- * one call must share one layout. */
-#define MOE_Q4_LAYOUT_ROWS  0
-#define MOE_Q4_LAYOUT_TILES 1
+ * one call must share one code-word order (ROWS, or TILES / TILES_SB); gate,
+ * up, sh_gate and sh_up must share one layout; TILES_SB is accepted for the
+ * gate and up matrices of every call (prefill and decode), not for down
+ * matrices (MOE_ERR_SHAPE); moe_dequant_q4_bf16 expands row-major code words
+ * only. */
+#define MOE_Q4_LAYOUT_ROWS     0
+#define MOE_Q4_LAYOUT_TILES    1
+#define MOE_Q4_LAYOUT_TILES_SB 2
 typedef struct {
     const uint32_t* codes;
     const uint16_t* scales;
@@ -120,7 +134,8 @@ typedef struct {
 
 /* Version of this ABI (bumped on any change of a signature or of a call's
  * requirements, such as the workspace it needs; 4: moe_route takes a
- * workspace for k = 4, 8 or 16 above 64 tokens). */
+ * workspace for k = 4, 8 or 16 above 64 tokens; 5: MOE_Q4_LAYOUT_TILES_SB
+ * and moe_q4_pack_scales). */
 int moe_abi_version(void);
 
 /* Human-readable text of a status code (static string; never NULL). */
@@ -281,6 +296,16 @@ int moe_router(const uint16_t* x, int T, int H, const uint16_t* w_router, int E,
  * matrix for later calls is {dst, src scales, src biases, MOE_Q4_LAYOUT_TILES}. */
 int moe_q4_prepack(const uint32_t* src_codes, int n_exp, int N, int K, uint32_t* dst_codes,
                    hipStream_t stream);
+
+/* Load time: the scales and biases of a matrix set [n_exp, N, K] (bf16
+ * [n_exp, N, K/64] each, row-major) packed into the MOE_Q4_LAYOUT_TILES_SB
+ * order: dst[((n/64)*(K/64) + g)*64 + n%64] = scale bits | bias bits << 16
+ * for global row n = e*N + n' and group g.  dst: device, n_exp*N*K/64 words,
+ * 4-byte aligned, distinct from the sources; N and K multiples of 64,
+ * n_exp*N*K/64 < 2^31.  Enqueues one kernel; with moe_q4_prepack's codes the
+ * matrix for later calls is {dst codes, dst, NULL, MOE_Q4_LAYOUT_TILES_SB}. */
+int moe_q4_pack_scales(const uint16_t* scales, const uint16_t* biases, int n_exp, int N, int K,
+                       uint32_t* dst, hipStream_t stream);
 
 /* Streaming-read probe (measurement only): reads `bytes` of `buf` once with
  * 16-byte loads, one contiguous 32 KB range per workgroup, and writes the

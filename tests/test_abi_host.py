@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert bq.abi_version() == 4
+    assert bq.abi_version() == 5
     for st, txt in [(0, "ok"), (-1, "null pointer"), (-2, "bad shape"), (-3, "misaligned pointer"),
                     (-4, "workspace too small"), (-5, "HIP launch error"), (-6, "unimplemented"),
                     (-99, "unknown status")]:
@@ -331,3 +331,38 @@ def test_chunked_driver_checks_the_chunk_shape_not_the_prompt():
     assert L.moe_layer_chunked(*args(T, 65536, 1 << 40)) == bq.MOE_ERR_SHAPE
     # the routing bound T*k < 2^30 holds for the whole prompt
     assert L.moe_layer_chunked(*args(1 << 27, 2048, 1 << 40)) == bq.MOE_ERR_SHAPE
+
+
+def test_packed_scale_layout_rules():
+    """MOE_Q4_LAYOUT_TILES_SB: biases may be NULL and the packed words need 4-byte alignment;
+    gate-side matrices share one layout, down matrices are never packed-scale, and all share
+    one code-word order.  moe_q4_pack_scales' argument checks.  Host only: every call stops
+    at a check (valid combinations at the workspace size)."""
+    L = bq.lib()
+    T, H, I, I_sh, E, k, br = 64, 256, 128, 128, 16, 2, 32
+    sb = bq.MoeQ4Mat(256, 256, None, bq.LAYOUT_TILES_SB)
+    tiles = bq.MoeQ4Mat(256, 256, 256, bq.LAYOUT_TILES)
+    rows = bq.MoeQ4Mat(256, 256, 256, bq.LAYOUT_ROWS)
+    r = bq.MoeRouting(*([16] * 9))
+    by = ctypes.byref
+
+    def gemm(g, d, sg, sd):
+        return L.moe_grouped_gemm_q4(256, T, H, I, I_sh, E, k, br, by(r), by(g), by(g), by(d),
+                                     by(sg), by(sg), by(sd), 256, 256, 256, 0, None)
+    assert gemm(sb, tiles, sb, tiles) == bq.MOE_ERR_WORKSPACE
+    assert gemm(tiles, tiles, tiles, tiles) == bq.MOE_ERR_WORKSPACE
+    assert gemm(sb, sb, sb, sb) == bq.MOE_ERR_SHAPE          # down matrices are not packed
+    assert gemm(sb, rows, sb, rows) == bq.MOE_ERR_SHAPE      # code-word orders differ
+    assert gemm(sb, tiles, tiles, tiles) == bq.MOE_ERR_SHAPE  # gate/up and shared gate/up differ
+    assert gemm(bq.MoeQ4Mat(256, 258, None, bq.LAYOUT_TILES_SB), tiles, sb, tiles) == bq.MOE_ERR_ALIGN
+    assert gemm(bq.MoeQ4Mat(256, 256, None, bq.LAYOUT_TILES), tiles, sb, tiles) == bq.MOE_ERR_NULL
+    assert gemm(bq.MoeQ4Mat(256, 256, 256, 3), tiles, sb, tiles) == bq.MOE_ERR_SHAPE
+
+    P = L.moe_q4_pack_scales
+    assert P(256, 512, 1, 60, 64, 1024, None) == bq.MOE_ERR_SHAPE      # N not a multiple of 64
+    assert P(256, 512, 1, 64, 96, 1024, None) == bq.MOE_ERR_SHAPE      # K not a multiple of 64
+    assert P(None, 512, 1, 64, 64, 1024, None) == bq.MOE_ERR_NULL
+    assert P(256, 512, 1, 64, 64, None, None) == bq.MOE_ERR_NULL
+    assert P(256, 512, 1, 64, 64, 256, None) == bq.MOE_ERR_SHAPE       # in place over the scales
+    assert P(256, 512, 1, 64, 64, 1026, None) == bq.MOE_ERR_ALIGN
+    assert P(256, 512, 1 << 16, 1 << 12, 1 << 12, 1024, None) == bq.MOE_ERR_SHAPE   # >= 2^31 words

@@ -48,9 +48,11 @@ def _probe_weights(H, I, seed):
     return LayerWeights(g, u, d, None, None, None)
 
 
-@pytest.mark.parametrize("H,I,block_rows", [(256, 128, 32), (512, 256, 16), (2048, 512, 64),
-                                             (2048, 512, 32)])
-def test_one_hot_probe_bit_exact(H, I, block_rows):
+@pytest.mark.parametrize("H,I,block_rows,prepack", [(256, 128, 32, False), (512, 256, 16, False),
+                                                     (2048, 512, 64, False), (2048, 512, 32, False),
+                                                     (2048, 512, 32, True), (512, 256, 16, True)])
+def test_one_hot_probe_bit_exact(H, I, block_rows, prepack):
+    """prepack: tile-packed codes with packed gate/up scale|bias words."""
     T = 96
     w = _probe_weights(H, I, seed=H + I)
     x = np.zeros((T, H), np.float32)
@@ -59,8 +61,8 @@ def test_one_hot_probe_bit_exact(H, I, block_rows):
     x_bits = f32_to_bf16_bits(x)
     logits = np.zeros((T, 1), np.float32)
     cfg = small_config(T, H, I, 1, 1, 0)
-    announce(f"one-hot probe H={H} I={I} br={block_rows}")
-    layer = bq.MoeLayer(w, H, I, 0, 1, 1, DEV, block_rows=block_rows)
+    announce(f"one-hot probe H={H} I={I} br={block_rows} prepack={prepack}")
+    layer = bq.MoeLayer(w, H, I, 0, 1, 1, DEV, block_rows=block_rows, prepack=prepack)
     got = run_layer(layer, x_bits, logits)
     ref = oracle_layer(w, cfg, x_bits, logits, block_rows)
     want = oracle.f32_to_bf16_rne_bits(ref["y"].astype(np.float32))

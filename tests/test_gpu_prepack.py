@@ -1,7 +1,9 @@
-"""Tile-packed code words (moe_q4_prepack): the repack is exactly the
-permutation the header documents, and every output of the layer, of decode
-and of the split phases is bit-identical to the row-major layout's (only the
-addresses of the code words change, not the arithmetic or its order)."""
+"""Tile-packed code words (moe_q4_prepack) and packed scale|bias words
+(moe_q4_pack_scales): each repack is exactly the permutation the header
+documents, and every output of the layer and of decode is bit-identical in
+the three layouts (row-major; tile-packed codes; tile-packed codes with packed
+gate/up scale|bias words): only the addresses change, not the arithmetic or
+its order."""
 import numpy as np
 import pytest
 import torch
@@ -45,6 +47,29 @@ def test_prepack_is_the_documented_permutation(n_exp, N, K):
     assert np.array_equal(np.sort(got), np.sort(codes.reshape(-1)))
 
 
+@pytest.mark.parametrize("n_exp,N,K", [(3, 128, 192), (2, 64, 64), (1, 512, 2048)])
+def test_pack_scales_is_the_documented_order(n_exp, N, K):
+    """dst[((n/64)*(K/64) + g)*64 + n%64] = scale bits | bias bits << 16, n = e*N + n'."""
+    rng = np.random.default_rng(N * 3 + K)
+    G = K // 64
+    sc = rng.integers(0, 2 ** 16, (n_exp, N, G), dtype=np.uint16)
+    bi = rng.integers(0, 2 ** 16, (n_exp, N, G), dtype=np.uint16)
+    s_d = torch.from_numpy(sc.view(np.int16)).to(DEV)
+    b_d = torch.from_numpy(bi.view(np.int16)).to(DEV)
+    dst = torch.zeros((n_exp, N, G), dtype=torch.int32, device=DEV)
+    announce(f"pack scales {n_exp}x{N}x{K}")
+    assert bq.lib().moe_q4_pack_scales(s_d.data_ptr(), b_d.data_ptr(), n_exp, N, K,
+                                       dst.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint32).reshape(-1)
+    rows = np.arange(n_exp * N)
+    n, g = np.meshgrid(rows, np.arange(G), indexing="ij")
+    want = np.empty(n_exp * N * G, np.uint32)
+    want[((n // 64) * G + g) * 64 + n % 64] = (sc.reshape(-1, G).astype(np.uint32)
+                                              | (bi.reshape(-1, G).astype(np.uint32) << 16))
+    assert np.array_equal(got, want)
+
+
 SHAPES = [
     # T,   H,    I,   E,  k, I_sh, block_rows
     (64, 256, 128, 16, 2, 128, 32),
@@ -62,24 +87,35 @@ def test_layer_outputs_identical_in_both_layouts(T, H, I, E, k, I_sh, block_rows
     w = make_weights(cfg, seed=T + H + 1, cache=False)
     x_bits, logits = make_activations(cfg)
     rows = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=block_rows)
-    tiles = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=block_rows, prepack=True)
+    tiles = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=block_rows, prepack="codes")
+    packed = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=block_rows, prepack=True)
     assert tiles.gate.layout == bq.LAYOUT_TILES
+    assert packed.gate.layout == bq.LAYOUT_TILES_SB and packed.down.layout == bq.LAYOUT_TILES
     announce(f"layouts T={T} H={H} I={I} E={E} k={k} I_sh={I_sh} br={block_rows}")
     a = run_layer(rows, x_bits, logits)
-    b = run_layer(tiles, x_bits, logits)
-    for key in ("y", "expert_out") + (("shared_out",) if I_sh else ()):
-        assert np.array_equal(a[key], b[key]), key
-    # decode: token by token through the two-launch path
+    for L in (tiles, packed):
+        b = run_layer(L, x_bits, logits)
+        for key in ("y", "expert_out") + (("shared_out",) if I_sh else ()):
+            assert np.array_equal(a[key], b[key]), (L.gate.layout, key)
+    # decode: token by token through the two-launch path (MoeLayer.decode gives the packed
+    # layer's plain-scale view; the packed matrices are also passed to moe_decode_q4 as is)
+    ws = torch.empty(bq.decode_workspace_bytes(H, I, I_sh, E, k), dtype=torch.uint8, device=DEV)
     for t in (0, T - 1):
         ys = []
-        for L in (rows, tiles):
-            x = bq.bf16_from_bits(x_bits[t:t + 1], DEV)
-            lg = torch.from_numpy(np.ascontiguousarray(logits[t:t + 1])).to(DEV)
+        x = bq.bf16_from_bits(x_bits[t:t + 1], DEV)
+        lg = torch.from_numpy(np.ascontiguousarray(logits[t:t + 1])).to(DEV)
+        for L in (rows, tiles, packed):
             y = torch.empty((1, H), dtype=torch.bfloat16, device=DEV)
             L.decode(x, lg, y)
             torch.cuda.synchronize()
             ys.append(bq.bf16_to_bits(y))
-        assert np.array_equal(ys[0], ys[1]), f"decode token {t}"
+        y = torch.empty((1, H), dtype=torch.bfloat16, device=DEV)
+        bq.moe_decode_q4(x, lg, I, I_sh, k, block_rows, *packed.weight_mats(), None, y, ws)
+        torch.cuda.synchronize()
+        ys.append(bq.bf16_to_bits(y))
+        assert np.array_equal(ys[0], ys[1]), f"decode token {t} (tiles)"
+        assert np.array_equal(ys[0], ys[2]), f"decode token {t} (packed layer, plain view)"
+        assert np.array_equal(ys[0], ys[3]), f"decode token {t} (packed scale|bias words)"
 
 
 @pytest.mark.parametrize("name", ["prefill512", "prefill2048"])
@@ -90,18 +126,21 @@ def test_prefill_identical_in_both_layouts(name):
     cfg = CONFIGS[name]
     w = make_weights(cfg, seed=0)
     rows = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
-    tiles = bq.MoeLayer.from_device([None if m is None else m.prepacked() for m in rows.weight_mats()],
+    tiles = bq.MoeLayer.from_device(bq.prepacked_mats(rows.weight_mats(), pack_scales=False),
                                     cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
+    packed = bq.MoeLayer.from_device(bq.prepacked_mats(rows.weight_mats()),
+                                     cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
     x_bits, logits = make_activations(cfg)
     announce(f"layouts {name}")
     a = run_layer(rows, x_bits, logits)
-    b = run_layer(tiles, x_bits, logits)
-    assert np.array_equal(a["y"], b["y"])
-    assert np.array_equal(a["expert_out"], b["expert_out"])
+    for L in (tiles, packed):
+        b = run_layer(L, x_bits, logits)
+        assert np.array_equal(a["y"], b["y"]), L.gate.layout
+        assert np.array_equal(a["expert_out"], b["expert_out"]), L.gate.layout
     # batch-1 decode over the same full-size weights, as the bench times it
     for t in (0, cfg.T // 2, cfg.T - 1):
         ys = []
-        for L in (rows, tiles):
+        for L in (rows, tiles, packed):
             xt = bq.bf16_from_bits(x_bits[t:t + 1], DEV)
             lg = torch.from_numpy(np.ascontiguousarray(logits[t:t + 1])).to(DEV)
             y = torch.empty((1, cfg.H), dtype=torch.bfloat16, device=DEV)
@@ -109,3 +148,4 @@ def test_prefill_identical_in_both_layouts(name):
             torch.cuda.synchronize()
             ys.append(bq.bf16_to_bits(y))
         assert np.array_equal(ys[0], ys[1]), f"decode token {t}"
+        assert np.array_equal(ys[0], ys[2]), f"decode token {t} (packed scales)"

@@ -37,8 +37,7 @@ def layers():
     cfg = CONFIGS["prefill512"]
     w = make_weights(cfg, seed=0)
     rows = bq.MoeLayer(w, cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
-    tiles = bq.MoeLayer.from_device([None if m is None else m.prepacked()
-                                     for m in rows.weight_mats()],
+    tiles = bq.MoeLayer.from_device(bq.prepacked_mats(rows.weight_mats()),
                                     cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
     torch.cuda.synchronize()
     return w, {"rows": rows, "tiles": tiles}
@@ -112,7 +111,7 @@ def _decode_tokens(layer_of, x_bits, logits, tokens, k, block_rows=32, graph=Fal
         for i, t in enumerate(tokens):
             L = layer_of(t)
             bq.moe_decode_q4(x[i:i + 1], lg[i:i + 1], L.I, L.I_sh, k, block_rows,
-                             *L.weight_mats(), None if graph else routes[i], y[i:i + 1], ws)
+                             *L.decode_mats(), None if graph else routes[i], y[i:i + 1], ws)
 
     if graph:
         calls()                                   # eager first: the replay must match it
@@ -162,8 +161,10 @@ def test_cold_decode_copies_from_a_graph(layers):
     base = L["tiles"]
     copies = [base] + [
         bq.MoeLayer.from_device(
-            [None if m is None else bq.DeviceQMat(m.codes ^ (0x01010101 * i), m.scales.clone(),
-                                                  m.biases.clone(), m.layout)
+            [None if m is None else bq.DeviceQMat(
+                m.codes ^ (0x01010101 * i), m.scales.clone(),
+                None if m.biases is None else m.biases.clone(), m.layout,
+                plain=None if m.plain is None else tuple(t.clone() for t in m.plain))
              for m in base.weight_mats()], cfg.H, cfg.I, cfg.I_sh, cfg.E, cfg.k, DEV)
         for i in range(1, 4)]
     tokens = list(range(64))
