@@ -118,6 +118,65 @@ def test_small_layer_parity(T, H, I, E, k, I_sh, br):
     assert_close_layer(got["y"], ref["y"])
 
 
+# Packed layers (tile-packed codes, packed gate/up scale|bias words) whose experts
+# average at least 48 rows: several full row blocks per expert and ragged last blocks,
+# the down GEMM on 64-row paired items, the shared expert over every token.
+LARGE_GROUPS = [
+    (301, 256, 128, 4, 2, 128, 32),       # ~150 rows per expert, T not a multiple of 64
+    (200, 128, 64, 4, 4, 64, 32),         # H = 128: one K-chunk
+    (301, 512, 128, 4, 2, 128, 32),
+    (200, 1024, 256, 4, 4, 256, 32),      # two gate/up column tiles
+    (520, 512, 128, 8, 1, 0, 32),         # no shared expert, ~65 rows per expert
+    (130, 512, 256, 2, 2, 128, 32),       # I_sh < I
+    (3000, 256, 128, 64, 8, 128, 32),     # above 2048 tokens
+    (97, 2048, 512, 2, 1, 512, 32),       # the layer's H and I; 97 shared rows: a ragged slot
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,I_sh,br", LARGE_GROUPS)
+def test_large_groups_parity_packed(T, H, I, E, k, I_sh, br):
+    assert T * k >= 48 * E
+    cfg = small_config(T, H, I, E, k, I_sh, seed=T + E + 5)
+    w = make_weights(cfg, seed=T * 7 + 3, cache=False)
+    x_bits, logits = make_activations(cfg)
+    announce(f"large groups, packed T={T} H={H} I={I} E={E} k={k} I_sh={I_sh}")
+    layer = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, block_rows=br, prepack=True)
+    got = run_layer(layer, x_bits, logits)
+    ref = oracle_layer(w, cfg, x_bits, logits, br)
+    assert_routing_matches(got["routing"], logits, k, br)
+    ok, ratio = tol_ok(bf16_bits_to_f64(got["expert_out"]), ref["expert_out"])
+    assert ok, f"expert_out {ratio:.3f}"
+    if I_sh:
+        ok, ratio = tol_ok(bf16_bits_to_f64(got["shared_out"]), ref["shared_out"])
+        assert ok, f"shared_out {ratio:.3f}"
+    assert_close_layer(got["y"], ref["y"])
+
+
+def test_one_expert_takes_every_token_packed():
+    """Packed layer, E = 8: expert 3 gets all 330 rows (ten full 32-row blocks and a
+    ragged eleventh; in the down GEMM five 64-row items and a 10-row leader), experts
+    5..7 stay empty."""
+    T, H, I, E, k, I_sh = 330, 512, 128, 8, 2, 128
+    cfg = small_config(T, H, I, E, k, I_sh, seed=81)
+    w = make_weights(cfg, seed=82, cache=False)
+    x_bits, logits = make_activations(cfg)
+    logits = logits.copy()
+    logits[:, 3] += np.float32(50.0)
+    logits[:, 5:] -= np.float32(50.0)
+    announce("one expert takes every token, packed")
+    layer = bq.MoeLayer(w, H, I, I_sh, E, k, DEV, prepack=True)
+    got = run_layer(layer, x_bits, logits)
+    assert int(got["routing"]["counts"][3]) == T
+    assert np.all(got["routing"]["counts"][5:] == 0)
+    ref = oracle_layer(w, cfg, x_bits, logits)
+    assert_routing_matches(got["routing"], logits, k)
+    ok, ratio = tol_ok(bf16_bits_to_f64(got["expert_out"]), ref["expert_out"])
+    assert ok, f"expert_out {ratio:.3f}"
+    ok, ratio = tol_ok(bf16_bits_to_f64(got["shared_out"]), ref["shared_out"])
+    assert ok, f"shared_out {ratio:.3f}"
+    assert_close_layer(got["y"], ref["y"])
+
+
 def test_one_expert_takes_every_token():
     """Expert 3's logit is raised for every token: it gets all T rows (10 full
     32-row blocks and a ragged 11th), the second choices spread over the rest,
