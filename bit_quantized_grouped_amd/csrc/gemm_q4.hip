@@ -485,9 +485,12 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
 // CG = WAVES * TPW * 32 output columns.  The block's h rows (MT x K bf16) are
 // staged in LDS once per item and every wave reads them; each wave owns TPW
 // tiles of 32 output columns over the whole K and requests all of their code
-// words right after the h rows and scales, so the item streams its weights in
-// one round of loads and the math on tile 0 starts while tile 1's words are
-// still arriving.  The product is
+// words right after the h rows, then its lanes' scales and biases, so the item
+// streams its weights in one round of loads and the math on tile 0 starts
+// while tile 1's words are still arriving.  A lane's scales and biases for a
+// tile are K / 128 consecutive groups of its weight row, loaded straight into
+// registers (8 bytes per array at K = 512): the item keeps no scale table in
+// LDS, which lets one more workgroup share a CU.  The product is
 // v_mfma_f32_32x32x16_bf16: lane half hf (lane / 32) takes the words of the
 // second half of K when hf = 1, so each lane reads half a weight row (K / 4
 // bytes) contiguously and its A elements come from the same K positions.
@@ -503,7 +506,6 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     constexpr int NT = WAVES * 64;
     constexpr int LDH = K + 8;            // h row stride in LDS, elements
     constexpr int G = KW;                 // scale groups per weight row
-    constexpr int GS = G + 2;             // scale row stride in LDS, elements
     constexpr int CG = WAVES * TPW * 32;  // output columns per item
     constexpr int CGS = CG + 8;           // output tile row stride in LDS
     constexpr int WPL = 4 * KW;           // code words per lane per tile (half a row)
@@ -512,8 +514,6 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
     static_assert(WAVES % 2 == 0, "tile-packed offsets assume 64-row steps per tile round");
     extern __shared__ __attribute__((aligned(16))) uint16_t smem_d[];
     uint16_t* sH = smem_d;                // [MT][LDH]
-    uint16_t* sSc = sH + MT * LDH;        // [CG][GS]
-    uint16_t* sBi = sSc + CG * GS;        // [CG][GS]
     uint16_t* sO = smem_d;                // [MT][CGS], after the math (aliases sH)
 
     const int tid = threadIdx.x;
@@ -563,24 +563,9 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
                              ra, (r0 + min(row, nr - 1)) * lda * 2 + c8 * 16, 0, 0));
         }
     }
-    // ---- scales and biases of the item's CG rows (rows past N read as zero) ----
-    constexpr int SP = CG * G / 8;                  // 16-byte pieces per array
-    constexpr int SPT = (SP + NT - 1) / NT;
-    const rsrc_t rs = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
-    const rsrc_t rb = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
-    u32x4_t vs[SPT], vb[SPT];
-#pragma unroll
-    for (int t = 0; t < SPT; ++t) {
-        const int pc = tid + NT * t;
-        if (SP % NT == 0 || pc < SP) {
-            const int vo = (n_base * G + pc * 8) * 2;
-            vs[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
-            vb[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, vo, 0, 0));
-        }
-    }
-    // ---- all code words of the wave's TPW tiles, requested after the h rows and
-    // scales so that the h stores below wait only for those; tile 0's math then
-    // starts while tile 1's words are still arriving ----
+    // ---- all code words of the wave's TPW tiles, requested after the h rows so
+    // that the h stores below wait only for those; tile 0's math then starts
+    // while tile 1's words are still arriving ----
     // Tile i of this wave covers output columns n_base + (i*WAVES + wave)*32 ..+32;
     // lane (n, hf) reads words hf*WPL .. +WPL of row (column) n of the tile,
     // KW loads of 4 words.  The per-(tile, load) step is uniform in both word
@@ -603,18 +588,28 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
             Bq[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, 0));
         }
     }
-
+    // ---- the lane's NGL groups of its weight row per tile (rows are G bf16 apart in
+    // the scale and bias arrays; tiles past N read zeros) ----
+    const rsrc_t rs = make_rsrc(q.scales + rows0 * G, (uint32_t)N * G * 2);
+    const rsrc_t rb = make_rsrc(q.biases + rows0 * G, (uint32_t)N * G * 2);
+    uint32_t lsc[TPW][(NGL + 1) / 2], lbi[TPW][(NGL + 1) / 2];
 #pragma unroll
-    for (int t = 0; t < SPT; ++t) {
-        const int pc = tid + NT * t;
-        if (SP % NT == 0 || pc < SP) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int flat = pc * 8 + e;
-                const int row = flat / G, g = flat % G;
-                sSc[row * GS + g] = (uint16_t)(vs[t][e / 2] >> (16 * (e & 1)));
-                sBi[row * GS + g] = (uint16_t)(vb[t][e / 2] >> (16 * (e & 1)));
-            }
+    for (int i = 0; i < TPW; ++i) {
+        const int row = n_base + (i * WAVES + wave) * 32 + n;
+        const int vo = (row * G + hf * WPL / 8) * 2 + (row < N ? 0 : kVoffOob);
+        if constexpr (NGL == 4) {
+            const u32x2_t a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, vo, 0, 0));
+            const u32x2_t b = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rb, vo, 0, 0));
+            lsc[i][0] = a[0];
+            lsc[i][1] = a[1];
+            lbi[i][0] = b[0];
+            lbi[i][1] = b[1];
+        } else if constexpr (NGL == 2) {
+            lsc[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, 0, 0);
+            lbi[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rb, vo, 0, 0);
+        } else {
+            lsc[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, 0, 0);
+            lbi[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rb, vo, 0, 0);
         }
     }
 #pragma unroll
@@ -639,13 +634,11 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][r][e] = 0.f;
         if (n_base + (i * WAVES + wave) * 32 >= N) continue;   // uniform per wave
-        const int col = (i * WAVES + wave) * 32 + n;            // within the item
         float sc[NGL], bi[NGL];
 #pragma unroll
         for (int gg = 0; gg < NGL; ++gg) {
-            const int gi = c0 / 8 + gg;
-            sc[gg] = bf16_to_f32(sSc[col * GS + gi]) * unit_inv;
-            bi[gg] = bf16_to_f32(sBi[col * GS + gi]);
+            sc[gg] = bf16_to_f32((uint16_t)(lsc[i][gg / 2] >> (16 * (gg & 1)))) * unit_inv;
+            bi[gg] = bf16_to_f32((uint16_t)(lbi[i][gg / 2] >> (16 * (gg & 1))));
         }
 #pragma unroll
         for (int j = 0; j < KW; ++j)
@@ -690,7 +683,7 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
 template <int KW, int TPW, int WAVES, int MT = 32>
 static size_t down_tiles_lds_bytes() {
     constexpr int K = KW * 64, CG = WAVES * TPW * 32;
-    const size_t a = (size_t)MT * (K + 8) * 2 + (size_t)2 * CG * (KW + 2) * 2;
+    const size_t a = (size_t)MT * (K + 8) * 2;
     const size_t o = (size_t)MT * (CG + 8) * 2;
     return a > o ? a : o;
 }
