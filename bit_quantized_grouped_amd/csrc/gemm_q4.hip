@@ -143,6 +143,32 @@ struct Streams {
 // loads it waits for all of them once per pass over the register ring).
 constexpr int kVoffOob = 0x40000000;
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes lds + 16 l
+// (lds wave-uniform).  The builtin exists only in the device pass.
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, void* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+// s_waitcnt vmcnt(n), leaving expcnt and lgkmcnt at their maxima (no wait on them).
+#define MOE_WAIT_VM(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// Workgroup barrier without a memory fence: the caller has already waited for
+// what the other waves must see (a fenced barrier would also wait for every
+// load still in flight into LDS).  The signal fences keep the compiler from
+// moving memory accesses across it, the scheduling barriers the scheduler.
+__device__ __forceinline__ void bare_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int NMAT, int NSUB, int KC, bool BF, bool SB>
 __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                        const Streams<NMAT, NSUB, KC>& S, int c, int voff_oob) {
@@ -186,7 +212,9 @@ __device__ __forceinline__ uint32_t word_of(const BChunk<NMAT, NSUB, W, BF>& B, 
 
 // sSc / sBi: this lane's row of bf16 scales / biases in LDS (row stride GS,
 // matrix stride mstride); grp = the group of the lane's words in this chunk.
-template <int NMAT, int MT, int KC, int NSUB, bool BF, bool SB>
+// XL: the A tile is dense (row stride KC) with 16-byte piece p of row r at
+// piece position p ^ (r % 16), as the direct-to-LDS x loads write it.
+template <int NMAT, int MT, int KC, int NSUB, bool BF, bool SB, bool XL = false>
 __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                               const uint16_t* sAc, const uint16_t* sSc,
                                               const uint16_t* sBi, int GS, int mstride, int grp,
@@ -221,7 +249,9 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, 
 #pragma unroll
         for (int mi = 0; mi < MT / 16; ++mi) {
             if (mi > 0 && mi >= msub_act) break;   // 16-row subtiles past the block's rows
-            const bf16x8_t a = *(const bf16x8_t*)(sAc + (mi * 16 + nl) * LDA + 8 * (g * W + j));
+            const bf16x8_t a =
+                XL ? *(const bf16x8_t*)(sAc + (mi * 16 + nl) * KC + 8 * ((g * W + j) ^ nl))
+                   : *(const bf16x8_t*)(sAc + (mi * 16 + nl) * LDA + 8 * (g * W + j));
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -251,6 +281,13 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     // LDS: [A buffer 0][A buffer 1][scale|bias pairs]; the output tile reuses it at the end
     extern __shared__ __attribute__((aligned(16))) uint16_t smem_g[];
     __shared__ int s_row[MT];
+    // XL (packed words, 128-K chunks): the x rows go straight from memory into a
+    // ring of three LDS tiles, two chunks ahead of their math, with no register
+    // staging; three separate arrays let the compiler tell their loads apart
+    constexpr bool XL = SB && KC == 128;
+    __shared__ __attribute__((aligned(16))) uint16_t sX0[XL ? MT * KC : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sX1[XL ? MT * KC : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sX2[XL ? MT * KC : 8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -419,42 +456,97 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     };
 
     const int nchunks = K / KC;
-    // Register pipeline over K-chunks: the A rows and code words of chunk c
-    // live in Aq/Bq[c % DEPTH] and are requested DEPTH-1 chunks before the
-    // chunk's math, so no load latency sits between two barriers.  A chunk c
-    // is staged into LDS buffer c % 2 one chunk ahead of its math.  Requests
-    // past the last chunk go out of bounds (kVoffOob) and are never used.
-    BChunk<NMAT, NSUB, W, BF> Bq[DEPTH];
-    u32x4_t Aq[DEPTH][APT];
+    if constexpr (XL) {
+        // Direct-to-LDS x rows: the tile of a chunk is MT rows x KC bf16, dense,
+        // written as 1 KB blocks (64 lanes x 16 B: RPB rows), block b by wave
+        // b % WAVES; lane l of a block writes piece position l % PPR of row
+        // b * RPB + l / PPR and fetches the row's piece (l % PPR) ^ (row % 16)
+        // (the XOR swizzle that keeps the MFMA fragment reads conflict-free).
+        // Chunk c goes to sX[c % 3], requested two chunks ahead, after the
+        // chunk's code words; every pipeline step issues NVM vector loads, so
+        // waiting for at most NVM outstanding at the end of step c means the
+        // x rows of chunk c + 1 (requested in step c - 1) have landed in every
+        // wave's part of the tile once the barrier is passed.
+        constexpr int PPR = KC / 8, RPB = 64 / PPR, NBLK = MT / RPB;
+        static_assert(NBLK % WAVES == 0, "whole 1 KB blocks per wave");
+        constexpr int APW = NBLK / WAVES;
+        constexpr int NB = NMAT * NSUB * 2;       // code-word and packed-word loads per chunk
+        constexpr int NVM = NB + APW;
+        int x_voff[APW];
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) {
-        const int oob = d < nchunks ? 0 : kVoffOob;
-        load_a(Aq[d], d, oob);
-        load_b<NMAT, NSUB, KC, BF, SB>(Bq[d], S, d, oob);
-    }
-    store_a(Aq[0], sA);
-    __syncthreads();
-    for (int c0 = 0; c0 < nchunks; c0 += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const int c = c0 + d;
-            const int cp = c + DEPTH - 1;
-            const int oob = cp < nchunks ? 0 : kVoffOob;
-            load_a(Aq[(d + DEPTH - 1) % DEPTH], cp, oob);
-            load_b<NMAT, NSUB, KC, BF, SB>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
-            if (c < nchunks) {
-                compute_chunk<NMAT, MT, KC, NSUB, BF, SB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane,
-                                                  sBi_lane, GS, mstride, c * KC / 64, unit_inv, nl,
-                                                  g, msub_act, acc);
-                // after the last chunk this stages unused data into the idle buffer
-                store_a(Aq[(d + 1) % DEPTH], sA + ((c + 1) & 1) * MT * LDA);
-            }
-            __syncthreads();
+        for (int i = 0; i < APW; ++i) {
+            const int row = (i * WAVES + wave) * RPB + lane / PPR;
+            x_voff[i] = s_row[row] * lda * 2 + (((lane % PPR) ^ (row % 16)) * 16);
         }
+        auto load_x = [&](uint16_t* buf, int c, int voff_oob) {
+#pragma unroll
+            for (int i = 0; i < APW; ++i)
+                buffer_load_lds16(a_rs, buf + (i * WAVES + wave) * 512, x_voff[i] + voff_oob,
+                                  c * KC * 2);
+        };
+        auto xbuf = [&](int i) { return i == 0 ? sX0 : (i == 1 ? sX1 : sX2); };
+        BChunk<NMAT, NSUB, W, BF> Bq[2];
+        load_b<NMAT, NSUB, KC, BF, SB>(Bq[0], S, 0, 0);
+        load_x(sX0, 0, 0);
+        load_x(sX1, 1, nchunks > 1 ? 0 : kVoffOob);
+        MOE_WAIT_VM(APW);
+        bare_barrier();
+        for (int c0 = 0; c0 < nchunks; c0 += 6) {
+#pragma unroll
+            for (int d = 0; d < 6; ++d) {
+                const int c = c0 + d;
+                load_b<NMAT, NSUB, KC, BF, SB>(Bq[(d + 1) % 2], S, c + 1,
+                                               c + 1 < nchunks ? 0 : kVoffOob);
+                load_x(xbuf((d + 2) % 3), c + 2, c + 2 < nchunks ? 0 : kVoffOob);
+                if (c < nchunks)
+                    compute_chunk<NMAT, MT, KC, NSUB, BF, SB, true>(
+                        Bq[d % 2], xbuf(d % 3), sSc_lane, sBi_lane, GS, mstride, c * KC / 64,
+                        unit_inv, nl, g, msub_act, acc);
+                MOE_WAIT_VM(NVM);
+                bare_barrier();
+            }
+        }
+        MOE_WAIT_VM(0);   // run-out loads write zeros into the ring: all land before sX0 is reused
+        bare_barrier();
+    } else {
+        // Register pipeline over K-chunks: the A rows and code words of chunk c
+        // live in Aq/Bq[c % DEPTH] and are requested DEPTH-1 chunks before the
+        // chunk's math, so no load latency sits between two barriers.  A chunk c
+        // is staged into LDS buffer c % 2 one chunk ahead of its math.  Requests
+        // past the last chunk go out of bounds (kVoffOob) and are never used.
+        BChunk<NMAT, NSUB, W, BF> Bq[DEPTH];
+        u32x4_t Aq[DEPTH][APT];
+    #pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d) {
+            const int oob = d < nchunks ? 0 : kVoffOob;
+            load_a(Aq[d], d, oob);
+            load_b<NMAT, NSUB, KC, BF, SB>(Bq[d], S, d, oob);
+        }
+        store_a(Aq[0], sA);
+        __syncthreads();
+        for (int c0 = 0; c0 < nchunks; c0 += DEPTH) {
+    #pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int c = c0 + d;
+                const int cp = c + DEPTH - 1;
+                const int oob = cp < nchunks ? 0 : kVoffOob;
+                load_a(Aq[(d + DEPTH - 1) % DEPTH], cp, oob);
+                load_b<NMAT, NSUB, KC, BF, SB>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
+                if (c < nchunks) {
+                    compute_chunk<NMAT, MT, KC, NSUB, BF, SB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane,
+                                                      sBi_lane, GS, mstride, c * KC / 64, unit_inv, nl,
+                                                      g, msub_act, acc);
+                    // after the last chunk this stages unused data into the idle buffer
+                    store_a(Aq[(d + 1) % DEPTH], sA + ((c + 1) & 1) * MT * LDA);
+                }
+                __syncthreads();
+            }
+        }
+
     }
 
     // ---- epilogue: bf16 tile [MT][COLS] in LDS, then 16-byte row stores ----
-    uint16_t* sO = smem_g;
+    uint16_t* sO = XL ? sX0 : smem_g;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
         const int col = (wave * NSUB + s) * 16 + nl;
@@ -694,6 +786,7 @@ template <int NMAT, int MT, int KC, int NSUB, int WAVES, bool SB = false>
 static size_t grouped_lds_bytes(int G, int wg_per_cu) {
     constexpr int LDA = KC + 8;
     constexpr int ROWS = WAVES * NSUB * 16;
+    if (SB && KC == 128) return 0;   // x rows in the kernel's static LDS ring
     const size_t a = (size_t)2 * MT * LDA * 2 + (SB ? 0 : (size_t)2 * NMAT * ROWS * (G + 8) * 2);
     const size_t o = (size_t)MT * ROWS * 2;
     size_t bytes = a > o ? a : o;
