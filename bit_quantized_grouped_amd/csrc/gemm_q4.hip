@@ -17,12 +17,17 @@
 // Data path per K-chunk of KC:
 //   A: the block's MT rows x KC bf16 are fetched DEPTH-1 chunks ahead into
 //      registers, then staged in LDS (double-buffered, row stride KC+8 so
-//      ds_read_b128 is conflict free) and read by every wave;
+//      ds_read_b128 is conflict free) and read by every wave.  With packed
+//      scale|bias words and 128-K chunks they go straight from memory into a
+//      3-tile LDS ring instead (buffer loads with the LDS flag, dense rows
+//      with XOR-swizzled 16-byte pieces), two chunks ahead;
 //   B: each lane streams KC/32 consecutive code words of each of its weight
 //      rows straight from HBM into registers with buffer loads (4 lanes
 //      cover a row's KC/2 bytes contiguously; the chunk and subtile offsets
 //      ride in the scalar offset, so no per-load address arithmetic),
-//      DEPTH-1 chunks ahead of the math.  Each word (8 weights) is dequantized
+//      DEPTH-1 chunks ahead of the math, with the row's scale|bias word of
+//      the chunk's group when the words are packed (else the scales and
+//      biases of the tile's rows sit in LDS).  Each word (8 weights) is dequantized
 //      in registers to bf16 and fed to v_mfma_f32_16x16x32_bf16.  A lane's 8
 //      weights are the 8 consecutive k of its word, so both operands use the
 //      natural K order inside each MFMA.
@@ -578,11 +583,12 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
 // staged in LDS once per item and every wave reads them; each wave owns TPW
 // tiles of 32 output columns over the whole K and requests all of their code
 // words right after the h rows, then its lanes' scales and biases, so the item
-// streams its weights in one round of loads and the math on tile 0 starts
-// while tile 1's words are still arriving.  A lane's scales and biases for a
-// tile are K / 128 consecutive groups of its weight row, loaded straight into
-// registers (8 bytes per array at K = 512): the item keeps no scale table in
-// LDS, which lets one more workgroup share a CU.  The product is
+// streams its weights in one round of loads (the math waits for that round:
+// a wave's words arrive as one burst, and requesting the scales first so that
+// tile 0 could start earlier measured no faster).  A lane's scales and biases
+// for a tile are K / 128 consecutive groups of its weight row, loaded straight
+// into registers (8 bytes per array at K = 512): the item keeps no scale table
+// in LDS, which lets one more workgroup share a CU.  The product is
 // v_mfma_f32_32x32x16_bf16: lane half hf (lane / 32) takes the words of the
 // second half of K when hf = 1, so each lane reads half a weight row (K / 4
 // bytes) contiguously and its A elements come from the same K positions.
@@ -656,8 +662,7 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiles_kernel(GroupedArgs p, i
         }
     }
     // ---- all code words of the wave's TPW tiles, requested after the h rows so
-    // that the h stores below wait only for those; tile 0's math then starts
-    // while tile 1's words are still arriving ----
+    // that the h stores below wait only for those ----
     // Tile i of this wave covers output columns n_base + (i*WAVES + wave)*32 ..+32;
     // lane (n, hf) reads words hf*WPL .. +WPL of row (column) n of the tile,
     // KW loads of 4 words.  The per-(tile, load) step is uniform in both word
@@ -781,7 +786,8 @@ static size_t down_tiles_lds_bytes() {
 }
 
 // Dynamic LDS bytes of one grouped_q4_kernel instance for K-groups G (with
-// packed scale|bias words, SB, there is no scale table).
+// packed scale|bias words, SB, there is no scale table, and with 128-K chunks
+// the A tiles live in the kernel's static LDS ring: nothing dynamic).
 template <int NMAT, int MT, int KC, int NSUB, int WAVES, bool SB = false>
 static size_t grouped_lds_bytes(int G, int wg_per_cu) {
     constexpr int LDA = KC + 8;
