@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 
@@ -32,14 +33,43 @@ def common_flags() -> list[str]:
     ]
 
 
+# Kernels whose pipeline waits count their own vector loads (s_waitcnt vmcnt with
+# a fixed count, then a barrier without a fence): the gate/up kernel on packed
+# scale|bias words with 128-K chunks, whose x rows go straight into LDS.  A
+# register spill would add scratch loads and stores to that count and turn the
+# waits into races, so the build fails if any of them uses scratch.
+COUNTED_WAIT_KERNELS = re.compile(r"grouped_q4_kernelILi2ELi\d+ELi128E.*Lb1EE")
+
+
+def check_no_scratch(remarks: str) -> int:
+    """Raise if a kernel matching COUNTED_WAIT_KERNELS reports scratch use; returns how
+    many such kernels the remarks list."""
+    name, seen = None, 0
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and COUNTED_WAIT_KERNELS.search(name):
+            seen += 1
+            if int(m.group(1)) != 0:
+                raise RuntimeError(f"{name} uses {m.group(1)} bytes of scratch per lane: its "
+                                   "counted load waits assume no spills")
+    return seen
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if src == "gemm_q4.hip" else []
+    cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    if extra and check_no_scratch(r.stderr) == 0:
+        raise RuntimeError("gemm_q4.hip: no counted-wait kernel in the resource remarks")
     return obj
 
 
