@@ -570,10 +570,34 @@ def main():
             xt, lgt = prep(c)
             settle(lambda: tiny.forward(xt, lgt), torch)
             mst = timed(lambda: tiny.forward(xt, lgt), max(20, args.steps), 10, torch)
+            # the same calls replayed from a captured graph: the GPU's time per call,
+            # without the host's per-call cost (which paces the eager loop at this size)
+            y_t = tiny.forward(xt, lgt)["y"]
+            torch.cuda.synchronize()
+            want = y_t.clone()
+            n_g = 20
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(n_g):
+                    tiny.forward(xt, lgt)
+            same = True
+            for _ in range(3):
+                y_t.zero_()
+                gr.replay()
+                torch.cuda.synchronize()
+                same = same and bool(torch.equal(y_t, want))
+            msg = timed(gr.replay, 10, 2, torch) / n_g
+            del gr
             extra["tiny"] = {"tokens_per_s": c.T / (mst * 1e-3), "us_per_call": mst * 1e3,
+                             "graph_us_per_call": msg * 1e3,
+                             "graph_tokens_per_s": c.T / (msg * 1e-3),
+                             "graph_matches_eager": same,
                              "what": "T 64, H 256, I 128, 16 experts top-2 + shared I 128: "
-                                     "launch-bound (four kernels for 1 MB of weights)"}
-            log(f"tiny: {mst*1e3:.1f} us/call, {c.T/(mst*1e-3):,.0f} tok/s")
+                                     "launch-bound (four kernels for 1 MB of weights); eager "
+                                     "calls from Python, and the same calls replayed from a "
+                                     "captured graph (each replay checked against eager)"}
+            log(f"tiny: {mst*1e3:.1f} us/call eager, {msg*1e3:.1f} us/call from a graph "
+                f"({c.T/(msg*1e-3):,.0f} tok/s; graph == eager: {same})")
             del tiny
         if not only or "prefill2048" in only:
             c = CONFIGS["prefill2048"]

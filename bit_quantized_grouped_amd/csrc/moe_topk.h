@@ -92,9 +92,11 @@ __device__ __forceinline__ void topk_rounds(uint32_t (&key)[EPL], int k, int32_t
 
 // Top-k of one token's E logits by one wave.  Lane l holds experts
 // l*EPL .. l*EPL+EPL-1.  s_key/s_e/s_v: this wave's LDS scratch of k entries
-// (used when k > kRoundsMaxK).
+// (used when k > kRoundsMaxK).  Always inlined: as an out-of-line call (which
+// the compiler chose for some EPL) it spilled registers to scratch and took
+// about 0.75 us per token.
 template <int EPL>
-__device__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* out_idx,
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* out_idx,
                            float* out_w, uint32_t* s_key, int* s_e, float* s_v,
                            int* lds_idx = nullptr) {
     const int lane = __lane_id();
