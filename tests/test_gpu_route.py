@@ -93,6 +93,22 @@ def test_route_chunk_match_path(T, E, k, levels, br, seed):
     assert_routing_matches(gpu_route(L, k, br), L, k, br)
 
 
+@pytest.mark.parametrize("T,E,k,levels,seed", [
+    (2048, 256, 8, 3, 21),     # 16384 assignments: the permutation built in LDS
+    (2049, 256, 8, 3, 22),     # one token more: written straight to memory
+    (8192, 64, 2, 4, 23),      # the grouping kernel without chunk information, at the limit
+    (8193, 64, 2, 4, 24),      # and above it
+    (300, 1000, 3, 5, 25),     # 1000 experts: largest histogram beside the LDS permutation
+])
+def test_route_sorted_permutation_staging(T, E, k, levels, seed):
+    """The grouping kernels build sorted_assign in LDS up to 16384 assignments and
+    write it out in order; above that they store it row by row.  Both sides of the
+    limit, with and without the chunk match information, match the oracle."""
+    L = _tie_heavy(T, E, levels, seed)
+    announce(f"route permutation staging T={T} E={E} k={k}")
+    assert_routing_matches(gpu_route(L, k, 32), L, k, 32)
+
+
 def test_route_all_equal_and_signed_zero():
     L = np.zeros((50, 32), np.float32)
     L[::2, 3] = np.float32(-0.0)
