@@ -99,6 +99,7 @@ def test_route_chunk_match_path(T, E, k, levels, br, seed):
     (8192, 64, 2, 4, 23),      # the grouping kernel without chunk information, at the limit
     (8193, 64, 2, 4, 24),      # and above it
     (300, 1000, 3, 5, 25),     # 1000 experts: largest histogram beside the LDS permutation
+    (2048, 1000, 8, 4, 26),    # both at their largest: 64 KB of histograms + 64 KB permutation
 ])
 def test_route_sorted_permutation_staging(T, E, k, levels, seed):
     """The grouping kernels build sorted_assign in LDS up to 16384 assignments and
