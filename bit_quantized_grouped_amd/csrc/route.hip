@@ -116,12 +116,24 @@ __device__ void block_exclusive_scan2(int a, int b, int* s_wave, int* ex_a, int*
     __syncthreads();
 }
 
+// LDS of the grouping pass, in ints: the per-wave histograms and the scan's
+// wave totals.
+__host__ __device__ constexpr int group_lds_ints(int E) {
+    return kGroupWaves * E + 2 * (kGroupWaves + 1);
+}
+
+// Blocks an expert's own thread writes into the block map; an expert with more
+// (a hot expert of a skewed batch: 60-odd blocks) has them written by its whole
+// wave, 64 at a time, instead of one thread's serial stores (3 us of a skewed
+// chunk's grouping).
+constexpr int kSerialBlocks = 8;
+
 // Per expert: prefix of the kGroupWaves segment counts in s_hist, totals
 // (counts), exclusive scan (offsets), the block map and n_blocks; afterwards
 // s_hist[w * E + e] holds the first row of segment w's assignments to e.
 __device__ void group_scan_block_map(int E, int block_rows, int max_blocks, const RoutingDev& r,
                                      int* s_hist) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid % WAVE;
     int* s_wave = s_hist + kGroupWaves * E;
     const int e = tid;
     int h[kGroupWaves];
@@ -136,15 +148,26 @@ __device__ void group_scan_block_map(int E, int block_rows, int max_blocks, cons
     if (e < E) {
         r.counts[e] = cnt;
         r.offsets[e] = off;
-        for (int i = 0; i < nb; ++i) {
-            r.block_expert[bstart + i] = e;
-            r.block_row[bstart + i] = off + block_rows * i;
+        if (nb <= kSerialBlocks) {
+            for (int i = 0; i < nb; ++i) {
+                r.block_expert[bstart + i] = e;
+                r.block_row[bstart + i] = off + block_rows * i;
+            }
         }
         int run = off;
 #pragma unroll
         for (int w = 0; w < kGroupWaves; ++w) {
             s_hist[w * E + e] = run;
             run += h[w];
+        }
+    }
+    for (uint64_t hot = __ballot(e < E && nb > kSerialBlocks); hot; hot &= hot - 1) {
+        const int src = __builtin_ctzll(hot);   // uniform: one hot expert of this wave
+        const int he = __shfl(e, src, WAVE), hb = __shfl(bstart, src, WAVE);
+        const int hn = __shfl(nb, src, WAVE), ho = __shfl(off, src, WAVE);
+        for (int i = lane; i < hn; i += WAVE) {
+            r.block_expert[hb + i] = he;
+            r.block_row[hb + i] = ho + block_rows * i;
         }
     }
     if (e == 0) {
@@ -410,7 +433,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_fused_kernel(
     extern __shared__ int smem_i[];
     const int wave = threadIdx.x / WAVE;
     int* s_hist = smem_i;                                  // kGroupWaves*E + 2*(kGroupWaves+1)
-    int* s_eids = s_hist + kGroupWaves * E + 2 * (kGroupWaves + 1);   // T*k
+    int* s_eids = s_hist + group_lds_ints(E);   // T*k
     uint32_t* s_scr = (uint32_t*)(s_eids + T * k) + wave * 3 * k;
     for (int t = wave; t < T; t += kGroupWaves) {
         topk_token<EPL>(logits + (size_t)t * E, E, k, r.topk_idx + (size_t)t * k,
@@ -422,7 +445,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_fused_kernel(
 }
 
 static size_t group_lds_bytes(int E) {
-    return (size_t)(kGroupWaves * E + 2 * (kGroupWaves + 1)) * sizeof(int);
+    return (size_t)group_lds_ints(E) * sizeof(int);
 }
 
 // The grouping-info kernel builds the permutation in LDS up to this many
