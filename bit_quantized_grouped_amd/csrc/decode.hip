@@ -33,8 +33,13 @@
 
 namespace moeq4 {
 
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = kDecThreads / WAVE;
+// waves of a gate/up workgroup (576 workgroups of 4: 2 or 3 per CU; 256 of 9, one
+// per CU with 18 row pairs each, measured 0.6 us per token slower)
+#ifndef MOE_DEC_GU_WAVES
+#define MOE_DEC_GU_WAVES 4
+#endif
+constexpr int kDecWaves = MOE_DEC_GU_WAVES;
+constexpr int kDecThreads = kDecWaves * WAVE;
 constexpr int kDecMaxK = 64;
 #ifndef MOE_DEC_GU_ROWS
 #define MOE_DEC_GU_ROWS 2
@@ -49,7 +54,8 @@ constexpr int kDnCols = 4;    // output columns per down workgroup (16 lanes eac
 #define MOE_DEC_DN_WAVES 8
 #endif
 // waves of a down workgroup; they split the k + 1 experts, so with 8 waves and
-// k = 8 only one wave streams two experts (8 beat 4 by 0.8 us per token, 12 tied, 16 lost)
+// k = 8 only one wave streams two experts (8 beat 4 by 0.8 us per token; 9, one
+// expert per wave, and 12 tied; 16 lost)
 constexpr int kDnWaves = MOE_DEC_DN_WAVES;
 constexpr int kDnThreads = kDnWaves * WAVE;
 
