@@ -174,17 +174,23 @@ __device__ __forceinline__ void bare_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int NMAT, int NSUB, int KC, bool BF, bool SB>
+// Cache-policy operand of a buffer load: the non-temporal hint (nt), which
+// inserts the lines as the first to be evicted.
+constexpr int kNonTemporal = 2;
+
+// STREAMED: the code and scale words are requested with the non-temporal hint.
+template <int NMAT, int NSUB, int KC, bool BF, bool SB, bool STREAMED = false>
 __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32, BF>& B,
                                        const Streams<NMAT, NSUB, KC>& S, int c, int voff_oob) {
     constexpr int W = KC / 32;
+    constexpr int CP = STREAMED ? kNonTemporal : 0;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
             if constexpr (SB)
                 B.sb[m][s] = __builtin_amdgcn_raw_buffer_load_b32(
-                    S.sbr[m], S.sb_off[s] + voff_oob, c * S.sb_chunk, 0);
+                    S.sbr[m], S.sb_off[s] + voff_oob, c * S.sb_chunk, CP);
             if constexpr (BF) {   // bf16 rows: K * 2 bytes; a chunk is KC * 2 bytes of a row
                 const int so_b = s * S.sub_c + c * (KC * 2);
 #pragma unroll
@@ -200,11 +206,11 @@ __device__ __forceinline__ void load_b(BChunk<NMAT, NSUB, KC / 32, BF>& B,
                 for (int j = 0; j < W / 4; ++j)
                     B.w[m][s][j] = __builtin_bit_cast(
                         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                     S.codes[m], S.voff_c + voff_oob + 16 * j, so_c, 0));
+                                     S.codes[m], S.voff_c + voff_oob + 16 * j, so_c, CP));
             } else {
                 B.w2[m][s] = __builtin_bit_cast(
                     u32x2_t,
-                    __builtin_amdgcn_raw_buffer_load_b64(S.codes[m], S.voff_c + voff_oob, so_c, 0));
+                    __builtin_amdgcn_raw_buffer_load_b64(S.codes[m], S.voff_c + voff_oob, so_c, CP));
             }
         }
 }
@@ -272,8 +278,10 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, 
 // each lane loads its row's word for the chunk's group with its code words,
 // so the workgroup keeps no scale table in LDS and preloads nothing (the
 // LDS holds only the A tiles, which lets more workgroups share a CU).
+// STREAMED: the weight words are requested with the non-temporal hint (chosen
+// per call when each expert's weights are read by about one row block).
 template <int NMAT, int MT, int KC, int NSUB, int DEPTH, int WAVES, bool BF = false,
-          bool SB = false>
+          bool SB = false, bool STREAMED = false>
 __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
     constexpr int NT = WAVES * 64;   // threads
     constexpr int W = KC / 32;       // code words per lane per chunk
@@ -491,7 +499,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         };
         auto xbuf = [&](int i) { return i == 0 ? sX0 : (i == 1 ? sX1 : sX2); };
         BChunk<NMAT, NSUB, W, BF> Bq[2];
-        load_b<NMAT, NSUB, KC, BF, SB>(Bq[0], S, 0, 0);
+        load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[0], S, 0, 0);
         load_x(sX0, 0, 0);
         load_x(sX1, 1, nchunks > 1 ? 0 : kVoffOob);
         MOE_WAIT_VM(APW);
@@ -500,7 +508,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
 #pragma unroll
             for (int d = 0; d < 6; ++d) {
                 const int c = c0 + d;
-                load_b<NMAT, NSUB, KC, BF, SB>(Bq[(d + 1) % 2], S, c + 1,
+                load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[(d + 1) % 2], S, c + 1,
                                                c + 1 < nchunks ? 0 : kVoffOob);
                 load_x(xbuf((d + 2) % 3), c + 2, c + 2 < nchunks ? 0 : kVoffOob);
                 if (c < nchunks)
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         for (int d = 0; d < DEPTH - 1; ++d) {
             const int oob = d < nchunks ? 0 : kVoffOob;
             load_a(Aq[d], d, oob);
-            load_b<NMAT, NSUB, KC, BF, SB>(Bq[d], S, d, oob);
+            load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[d], S, d, oob);
         }
         store_a(Aq[0], sA);
         __syncthreads();
@@ -536,7 +544,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
                 const int cp = c + DEPTH - 1;
                 const int oob = cp < nchunks ? 0 : kVoffOob;
                 load_a(Aq[(d + DEPTH - 1) % DEPTH], cp, oob);
-                load_b<NMAT, NSUB, KC, BF, SB>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
+                load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
                 if (c < nchunks) {
                     compute_chunk<NMAT, MT, KC, NSUB, BF, SB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane,
                                                       sBi_lane, GS, mstride, c * KC / 64, unit_inv, nl,
@@ -818,11 +826,11 @@ static int pick_kc(int K, int K2, int kc_max) {
     return 0;
 }
 
-template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES, bool BF, bool SB>
+template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES, bool BF, bool SB, bool STREAMED>
 static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_cu,
                       hipStream_t stream) {
 #define MOE_LAUNCH(KCV)                                                                          \
-    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES, BF, SB><<<                              \
+    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES, BF, SB, STREAMED><<<                    \
         grid, WAVES * 64, grouped_lds_bytes<NMAT, MT, KCV, NSUB, WAVES, SB>(G, wg_per_cu),        \
         stream>>>(a)
     if (kc == 256) MOE_LAUNCH(256);
@@ -831,16 +839,17 @@ static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_
 #undef MOE_LAUNCH
 }
 
-template <int NMAT, int NSUB, int DEPTH, int WAVES, bool BF = false, bool SB = false>
+template <int NMAT, int NSUB, int DEPTH, int WAVES, bool BF = false, bool SB = false,
+          bool STREAMED = false>
 static void launch_grouped(GroupedArgs a, int mt, int kc, int n_max, int slots, int G,
                            int wg_per_cu, hipStream_t stream) {
     constexpr int cols = WAVES * NSUB * 16;
     a.n_tiles = (n_max + cols - 1) / cols;
     const long long items = (long long)slots * a.n_tiles;
     const int grid = (int)((items + kXcds - 1) / kXcds) * kXcds;
-    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
-    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
-    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
+    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES, BF, SB, STREAMED>(a, kc, grid, G, wg_per_cu, stream);
+    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES, BF, SB, STREAMED>(a, kc, grid, G, wg_per_cu, stream);
+    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES, BF, SB, STREAMED>(a, kc, grid, G, wg_per_cu, stream);
 }
 
 static GroupedArgs common_args(const GemmProblem& p) {
@@ -905,9 +914,20 @@ static GroupedArgs down_args(const GemmProblem& p, const void* ws) {
 hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
     const GroupedArgs a = gateup_args(p, ws);
     if (p.gate.layout == 2) {   // packed scale|bias words: no LDS table, a shorter ring
-        launch_grouped<2, MOE_GU_NSUB, MOE_GU_SB_DEPTH, MOE_GU_WAVES, false, true>(
-            a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
-            a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
+        // When the experts average at most one row block (T * k <= E * block_rows),
+        // each routed weight tile is read about once: its words are requested as
+        // non-temporal, so the stream does not evict the x rows, h and the other
+        // data the call reuses.  With more rows per expert the blocks of one
+        // expert re-read its tiles from the caches, and the hint is left off.
+        const bool once = (long long)p.T * p.k <= (long long)p.E * p.block_rows;
+        if (once)
+            launch_grouped<2, MOE_GU_NSUB, MOE_GU_SB_DEPTH, MOE_GU_WAVES, false, true, true>(
+                a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
+                a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
+        else
+            launch_grouped<2, MOE_GU_NSUB, MOE_GU_SB_DEPTH, MOE_GU_WAVES, false, true, false>(
+                a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
+                a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
         return hipGetLastError();
     }
     launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES>(
