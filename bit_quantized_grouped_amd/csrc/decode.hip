@@ -170,11 +170,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int k = p.k, H = p.H, I = p.I, I_sh = p.I_sh;
 
-    // One pass of the grid covers every task, so this workgroup's rows are
-    // tasks [8b, 8b + 8): when they are all shared-expert rows it needs no
-    // top-k (workgroup 0 still computes it to publish the selection).
+    // Tasks are the k selected experts' rows (expert j's rows after expert
+    // j - 1's), then the shared expert's rows, whose workgroups need no top-k
+    // and start streaming at once.  They come last in the grid because the
+    // workgroups that share a CU with others finish in the order they were
+    // placed there, and the shared rows, streaming from the start, make the
+    // best last ones.  One pass of the grid covers every task, so this
+    // workgroup's rows are tasks [8b, 8b + 8) (workgroup 0 always selects, to
+    // publish the selection).
+    const int routed_tasks = k * I;
     const bool need_topk =
-        blockIdx.x == 0 || (int)(blockIdx.x + 1) * kDecWaves * kGuRows > I_sh;
+        blockIdx.x == 0 || (int)blockIdx.x * kDecWaves * kGuRows < routed_tasks;
     if (wave == 0 && need_topk)
         topk_token<EPL>(p.logits, p.E, k, s_idx, s_w, s_scr, (int*)(s_scr + k),
                         (float*)(s_scr + 2 * k), nullptr);
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
     }
 
     const int ldh = I > I_sh ? I : I_sh;
-    const int n_tasks = I_sh + k * I;   // shared-expert rows first, then expert j's rows
+    const int n_tasks = routed_tasks + I_sh;
     const float unit_inv = 1.0f / fp8_unit();
     const int stride = gridDim.x * kDecWaves * kGuRows;
     for (int t0 = (blockIdx.x * kDecWaves + wave) * kGuRows; t0 < n_tasks; t0 += stride) {
@@ -200,9 +206,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs p
 #pragma unroll
         for (int r = 0; r < kGuRows; ++r) {
             const int t = t0 + r < n_tasks ? t0 + r : n_tasks - 1;   // tail: re-read a valid row
-            const bool sh = t < I_sh;
-            const int j = sh ? k : (t - I_sh) / I;
-            const int n = sh ? t : (t - I_sh) - j * I;
+            const bool sh = t >= routed_tasks;
+            const int j = sh ? k : t / I;
+            const int n = sh ? t - routed_tasks : t - j * I;
             const size_t row = sh ? (size_t)n : (size_t)__builtin_amdgcn_readfirstlane(s_idx[j]) * I + n;
             const QMatDev& g = sh ? p.sh_gate : p.gate;
             const QMatDev& u = sh ? p.sh_up : p.up;
