@@ -33,8 +33,9 @@
 
 namespace moeq4 {
 
-// waves of a gate/up workgroup (576 workgroups of 4: 2 or 3 per CU; 256 of 9, one
-// per CU with 18 row pairs each, measured 0.6 us per token slower)
+// waves of a gate/up workgroup (576 workgroups of 4: 2 or 3 per CU; measured
+// slower: 256 of 9, one per CU with 18 row pairs each, by 0.6 us per token; 8
+// waves, the routed rows one workgroup per CU, by 0.2 us; 6 waves by 1.5 us)
 #ifndef MOE_DEC_GU_WAVES
 #define MOE_DEC_GU_WAVES 4
 #endif
