@@ -38,9 +38,9 @@ def common_flags() -> list[str]:
 # scale|bias words with 128-K chunks, whose x rows go straight into LDS.  A
 # register spill would add scratch loads and stores to that count and turn the
 # waits into races, so the build fails if any of them uses scratch.
-# Template arguments: NMAT 2, MT, KC 128, NSUB, DEPTH, WAVES, BF false, SB true, NT.
+# Template arguments: NMAT 2, MT, KC 128, NSUB, DEPTH, WAVES, BF false, SB true.
 COUNTED_WAIT_KERNELS = re.compile(
-    r"grouped_q4_kernelILi2ELi\d+ELi128ELi\d+ELi\d+ELi\d+ELb0ELb1ELb[01]EE")
+    r"grouped_q4_kernelILi2ELi\d+ELi128ELi\d+ELi\d+ELi\d+ELb0ELb1EE")
 
 
 def check_no_scratch(remarks: str) -> int:

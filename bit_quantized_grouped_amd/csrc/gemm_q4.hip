@@ -117,6 +117,12 @@ struct GroupedArgs {
 // consecutive blocks of one expert, then share an L2.
 constexpr int kXcds = 8;
 
+// A compile-time flag passed as a value (to instantiate a lambda body twice).
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 // One K-chunk of a lane's B operand: W code words per weight row (4-bit
 // weights), or, in the bf16-weight mode (BF), W x 8 bf16 weights per row.
 template <int NMAT, int NSUB, int W, bool BF = false>
@@ -278,11 +284,14 @@ __device__ __forceinline__ void compute_chunk(const BChunk<NMAT, NSUB, KC / 32, 
 // each lane loads its row's word for the chunk's group with its code words,
 // so the workgroup keeps no scale table in LDS and preloads nothing (the
 // LDS holds only the A tiles, which lets more workgroups share a CU).
-// STREAMED: the weight words are requested with the non-temporal hint (chosen
-// per call when each expert's weights are read by about one row block).
+// With packed words and 128-K chunks the kernel is held to 6 waves per SIMD:
+// its loop exists twice (weight words with or without the non-temporal hint),
+// which the register allocator would otherwise widen past that occupancy.
 template <int NMAT, int MT, int KC, int NSUB, int DEPTH, int WAVES, bool BF = false,
-          bool SB = false, bool STREAMED = false>
-__global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
+          bool SB = false>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(SB && KC == 128 ? 6 : 1, 8)))
+void grouped_q4_kernel(GroupedArgs p) {
     constexpr int NT = WAVES * 64;   // threads
     constexpr int W = KC / 32;       // code words per lane per chunk
     constexpr int MSUB = MT / 16;
@@ -498,8 +507,16 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
                                   c * KC * 2);
         };
         auto xbuf = [&](int i) { return i == 0 ? sX0 : (i == 1 ? sX1 : sX2); };
+        // The loop is instantiated for both cache policies of the weight words and
+        // the item picks one (a branch per load would cost more than the hint
+        // gains): non-temporal when this row block is its expert's only one, so
+        // the tile is read once and streams through without evicting the x rows
+        // and the data the rest of the call reuses; the default when other blocks
+        // of the expert read the same tiles from the caches.
+        auto xl_loop = [&](auto policy) {
+        constexpr bool ST = decltype(policy)::value;
         BChunk<NMAT, NSUB, W, BF> Bq[2];
-        load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[0], S, 0, 0);
+        load_b<NMAT, NSUB, KC, BF, SB, ST>(Bq[0], S, 0, 0);
         load_x(sX0, 0, 0);
         load_x(sX1, 1, nchunks > 1 ? 0 : kVoffOob);
         MOE_WAIT_VM(APW);
@@ -508,8 +525,8 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
 #pragma unroll
             for (int d = 0; d < 6; ++d) {
                 const int c = c0 + d;
-                load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[(d + 1) % 2], S, c + 1,
-                                               c + 1 < nchunks ? 0 : kVoffOob);
+                load_b<NMAT, NSUB, KC, BF, SB, ST>(Bq[(d + 1) % 2], S, c + 1,
+                                                   c + 1 < nchunks ? 0 : kVoffOob);
                 load_x(xbuf((d + 2) % 3), c + 2, c + 2 < nchunks ? 0 : kVoffOob);
                 if (c < nchunks)
                     compute_chunk<NMAT, MT, KC, NSUB, BF, SB, true>(
@@ -521,6 +538,11 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         }
         MOE_WAIT_VM(0);   // run-out loads write zeros into the ring: all land before sX0 is reused
         bare_barrier();
+        };
+        const bool read_once =
+            is_sh ? p.sh_blocks == 1 : p.offsets[expert + 1] - p.offsets[expert] <= MT;
+        if (read_once) xl_loop(BoolTag<true>{});
+        else xl_loop(BoolTag<false>{});
     } else {
         // Register pipeline over K-chunks: the A rows and code words of chunk c
         // live in Aq/Bq[c % DEPTH] and are requested DEPTH-1 chunks before the
@@ -533,7 +555,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
         for (int d = 0; d < DEPTH - 1; ++d) {
             const int oob = d < nchunks ? 0 : kVoffOob;
             load_a(Aq[d], d, oob);
-            load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[d], S, d, oob);
+            load_b<NMAT, NSUB, KC, BF, SB>(Bq[d], S, d, oob);
         }
         store_a(Aq[0], sA);
         __syncthreads();
@@ -544,7 +566,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_q4_kernel(GroupedArgs p) {
                 const int cp = c + DEPTH - 1;
                 const int oob = cp < nchunks ? 0 : kVoffOob;
                 load_a(Aq[(d + DEPTH - 1) % DEPTH], cp, oob);
-                load_b<NMAT, NSUB, KC, BF, SB, STREAMED>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
+                load_b<NMAT, NSUB, KC, BF, SB>(Bq[(d + DEPTH - 1) % DEPTH], S, cp, oob);
                 if (c < nchunks) {
                     compute_chunk<NMAT, MT, KC, NSUB, BF, SB>(Bq[d], sA + (c & 1) * MT * LDA, sSc_lane,
                                                       sBi_lane, GS, mstride, c * KC / 64, unit_inv, nl,
@@ -826,11 +848,11 @@ static int pick_kc(int K, int K2, int kc_max) {
     return 0;
 }
 
-template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES, bool BF, bool SB, bool STREAMED>
+template <int NMAT, int MT, int NSUB, int DEPTH, int WAVES, bool BF, bool SB>
 static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_cu,
                       hipStream_t stream) {
 #define MOE_LAUNCH(KCV)                                                                          \
-    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES, BF, SB, STREAMED><<<                    \
+    grouped_q4_kernel<NMAT, MT, KCV, NSUB, DEPTH, WAVES, BF, SB><<<                              \
         grid, WAVES * 64, grouped_lds_bytes<NMAT, MT, KCV, NSUB, WAVES, SB>(G, wg_per_cu),        \
         stream>>>(a)
     if (kc == 256) MOE_LAUNCH(256);
@@ -839,17 +861,16 @@ static void launch_mt(const GroupedArgs& a, int kc, int grid, int G, int wg_per_
 #undef MOE_LAUNCH
 }
 
-template <int NMAT, int NSUB, int DEPTH, int WAVES, bool BF = false, bool SB = false,
-          bool STREAMED = false>
+template <int NMAT, int NSUB, int DEPTH, int WAVES, bool BF = false, bool SB = false>
 static void launch_grouped(GroupedArgs a, int mt, int kc, int n_max, int slots, int G,
                            int wg_per_cu, hipStream_t stream) {
     constexpr int cols = WAVES * NSUB * 16;
     a.n_tiles = (n_max + cols - 1) / cols;
     const long long items = (long long)slots * a.n_tiles;
     const int grid = (int)((items + kXcds - 1) / kXcds) * kXcds;
-    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES, BF, SB, STREAMED>(a, kc, grid, G, wg_per_cu, stream);
-    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES, BF, SB, STREAMED>(a, kc, grid, G, wg_per_cu, stream);
-    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES, BF, SB, STREAMED>(a, kc, grid, G, wg_per_cu, stream);
+    if (mt == 16) launch_mt<NMAT, 16, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
+    else if (mt == 32) launch_mt<NMAT, 32, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
+    else launch_mt<NMAT, 64, NSUB, DEPTH, WAVES, BF, SB>(a, kc, grid, G, wg_per_cu, stream);
 }
 
 static GroupedArgs common_args(const GemmProblem& p) {
@@ -914,20 +935,9 @@ static GroupedArgs down_args(const GemmProblem& p, const void* ws) {
 hipError_t launch_gateup(const GemmProblem& p, void* ws, hipStream_t stream) {
     const GroupedArgs a = gateup_args(p, ws);
     if (p.gate.layout == 2) {   // packed scale|bias words: no LDS table, a shorter ring
-        // When the experts average at most one row block (T * k <= E * block_rows),
-        // each routed weight tile is read about once: its words are requested as
-        // non-temporal, so the stream does not evict the x rows, h and the other
-        // data the call reuses.  With more rows per expert the blocks of one
-        // expert re-read its tiles from the caches, and the hint is left off.
-        const bool once = (long long)p.T * p.k <= (long long)p.E * p.block_rows;
-        if (once)
-            launch_grouped<2, MOE_GU_NSUB, MOE_GU_SB_DEPTH, MOE_GU_WAVES, false, true, true>(
-                a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
-                a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
-        else
-            launch_grouped<2, MOE_GU_NSUB, MOE_GU_SB_DEPTH, MOE_GU_WAVES, false, true, false>(
-                a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
-                a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
+        launch_grouped<2, MOE_GU_NSUB, MOE_GU_SB_DEPTH, MOE_GU_WAVES, false, true>(
+            a, p.block_rows, pick_kc(p.H, 0, MOE_GU_KC), p.I > p.I_sh ? p.I : p.I_sh,
+            a.sh_blocks + p.max_blocks, p.H / 64, MOE_GU_WG_PER_CU, stream);
         return hipGetLastError();
     }
     launch_grouped<2, MOE_GU_NSUB, MOE_GU_DEPTH, MOE_GU_WAVES>(

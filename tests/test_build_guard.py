@@ -5,8 +5,8 @@ import pytest
 
 from bit_quantized_grouped_amd import build
 
-NAME = "_ZN5moeq417grouped_q4_kernelILi2ELi32ELi128ELi1ELi2ELi4ELb0ELb1ELb0EEEvNS_11GroupedArgsE"
-NAME_NT = NAME.replace("ELb0ELb1ELb0EE", "ELb0ELb1ELb1EE")   # non-temporal weight words
+NAME = "_ZN5moeq417grouped_q4_kernelILi2ELi32ELi128ELi1ELi2ELi4ELb0ELb1EEEvNS_11GroupedArgsE"
+NAME_MT16 = NAME.replace("ELi32ELi128E", "ELi16ELi128E")   # 16-row blocks
 
 
 def remarks(name, scratch):
@@ -16,12 +16,12 @@ def remarks(name, scratch):
             f"[-Rpass-analysis=kernel-resource-usage]\n")
 
 
-@pytest.mark.parametrize("name", [NAME, NAME_NT])
+@pytest.mark.parametrize("name", [NAME, NAME_MT16])
 def test_counted_wait_kernel_without_scratch_passes(name):
     assert build.check_no_scratch(remarks(name, 0)) == 1
 
 
-@pytest.mark.parametrize("name", [NAME, NAME_NT])
+@pytest.mark.parametrize("name", [NAME, NAME_MT16])
 def test_counted_wait_kernel_with_scratch_fails(name):
     with pytest.raises(RuntimeError, match="scratch"):
         build.check_no_scratch(remarks(name, 16))
@@ -29,8 +29,8 @@ def test_counted_wait_kernel_with_scratch_fails(name):
 
 @pytest.mark.parametrize("other", [
     NAME.replace("ELi128E", "ELi64E"),        # 64-K chunks: register-staged x rows
-    NAME.replace("ELb0ELb1ELb0E", "ELb0ELb0ELb0E"),   # separate scale arrays
-    NAME.replace("ELb0ELb1ELb0E", "ELb1ELb0ELb0E"),   # bf16-weight baseline
+    NAME.replace("ELb0ELb1E", "ELb0ELb0E"),   # separate scale arrays
+    NAME.replace("ELb0ELb1E", "ELb1ELb0E"),   # bf16-weight baseline
     "_ZN5moeq418route_fused_kernelILi1EEEvPKfiiiiiNS_10RoutingDevE",
 ])
 def test_other_kernels_are_not_guarded(other):
