@@ -33,17 +33,18 @@
 
 namespace moeq4 {
 
-// waves of a gate/up workgroup (576 workgroups of 4: 2 or 3 per CU; measured
-// slower: 256 of 9, one per CU with 18 row pairs each, by 0.6 us per token; 8
-// waves, the routed rows one workgroup per CU, by 0.2 us; 6 waves by 1.5 us)
+// Gate/up shape: waves per workgroup x row pairs per wave.  8 x 1 (576
+// workgroups, one top-k per 8 rows) measured fastest with the shared rows last:
+// 11.9 us per token against 12.0 for 4 x 1, 12.3 for 4 x 2, 12.5 for 8 x 2,
+// 12.6 for 12 x 1, 13.4 for 2 x 1 and 14.9 for 16 x 1.
 #ifndef MOE_DEC_GU_WAVES
-#define MOE_DEC_GU_WAVES 4
+#define MOE_DEC_GU_WAVES 8
 #endif
 constexpr int kDecWaves = MOE_DEC_GU_WAVES;
 constexpr int kDecThreads = kDecWaves * WAVE;
 constexpr int kDecMaxK = 64;
 #ifndef MOE_DEC_GU_ROWS
-#define MOE_DEC_GU_ROWS 2
+#define MOE_DEC_GU_ROWS 1
 #endif
 #ifndef MOE_DEC_DN_EXP
 #define MOE_DEC_DN_EXP 1
