@@ -53,11 +53,11 @@ constexpr int kGuRows = MOE_DEC_GU_ROWS;   // gate/up row pairs one wave streams
 constexpr int kDnExp = MOE_DEC_DN_EXP;     // experts whose down rows one wave loads together
 constexpr int kDnCols = 4;    // output columns per down workgroup (16 lanes each)
 #ifndef MOE_DEC_DN_WAVES
-#define MOE_DEC_DN_WAVES 8
+#define MOE_DEC_DN_WAVES 9
 #endif
-// waves of a down workgroup; they split the k + 1 experts, so with 8 waves and
-// k = 8 only one wave streams two experts (8 beat 4 by 0.8 us per token; 9, one
-// expert per wave, and 12 tied; 16 lost)
+// waves of a down workgroup; they split the k + 1 experts, one each at k = 8
+// (with the 8 x 1 gate/up shape: 9 and 12 waves 12.2 us per token cold, 8 waves
+// 12.4, 4 waves 13.2, 16 waves 13.8)
 constexpr int kDnWaves = MOE_DEC_DN_WAVES;
 constexpr int kDnThreads = kDnWaves * WAVE;
 
